@@ -1,0 +1,184 @@
+"""Seeded generators for attention inputs with block-structured score mass.
+
+Every generator uses ``numpy.random.default_rng(seed)`` (PCG64) and draws in a
+fixed order so a seed names one exact tensor set.  Values are drawn in fp32 and,
+for bf16 workloads, rounded once to bf16 with round-to-nearest-even (torch's
+CPU cast).  Whatever consumes the tensors (the fp64 oracle, the GPU kernels)
+reads back exactly those rounded values.
+
+Two families:
+
+* ``clustered_*`` -- keys sit near unit-norm centroids, one centroid per
+  128-key tile, so a query near a few centroids scores high on a few tiles and
+  low on the rest: the regime in which whole key tiles carry negligible
+  softmax mass.
+* ``video_dit_field`` -- queries and keys sampled from spatially smooth 3-D
+  fields over a (frames, height, width) latent grid plus a bounded locality
+  term, so nearby tokens score high: a stand-in for video diffusion
+  transformer self-attention.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+TILE = 128  # keys per tile that a centroid is assigned to
+
+
+def bf16_round(x: np.ndarray) -> torch.Tensor:
+    """fp32 array -> contiguous bf16 CPU tensor (round to nearest even)."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def _to_tensor(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return bf16_round(x)
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _torch_dtype(dtype: str) -> torch.dtype:
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+
+
+def _centroids(rng: np.random.Generator, n_c: int, d: int) -> np.ndarray:
+    c = rng.standard_normal((n_c, d), dtype=np.float32)
+    c /= np.linalg.norm(c, axis=1, keepdims=True)
+    return c
+
+
+def clustered_prefill(seed: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, D: int,
+                      Dv: int, n_c: int, r: float, query_mode: str, dtype: str = "bf16",
+                      sigma: float = 0.5) -> dict:
+    """Tile-clustered Q/K/V for a prefill call.
+
+    Draw order: centroids ``C`` (n_c x D, row-normalised); then for each
+    (b, kv head) in order: tile centroids ``z`` (one per 128-key tile), key
+    noise, query centroid choices (``query_mode == "row"`` only), query noise
+    for the ``Hq/Hkv`` heads of the group, then V ~ N(0, 1).
+
+    ``k = r*C[z_tile] + sigma*eps``.  Queries:
+
+    * ``"row"``: every query row of every head picks its own centroid
+      uniformly, ``q = r*C[zq] + sigma*eps``;
+    * ``"tile"``: self-attention layout -- query position ``p`` uses the
+      centroid of the key tile holding key position ``p + Lk - Lq`` (clamped
+      to the key range), with independent noise per head.
+    """
+    rng = np.random.default_rng(seed)
+    g = Hq // Hkv
+    nK = -(-Lk // TILE)
+    C = _centroids(rng, n_c, D)
+    tdt = _torch_dtype(dtype)
+    q = torch.empty((B, Hq, Lq, D), dtype=tdt)
+    k = torch.empty((B, Hkv, Lk, D), dtype=tdt)
+    v = torch.empty((B, Hkv, Lk, Dv), dtype=tdt)
+    key_tile_of_query = np.clip(np.arange(Lq) + (Lk - Lq), 0, Lk - 1) // TILE
+    for b in range(B):
+        for hk in range(Hkv):
+            z = rng.integers(0, n_c, size=nK)
+            kz = np.repeat(z, TILE)[:Lk]
+            kk = r * C[kz] + sigma * rng.standard_normal((Lk, D), dtype=np.float32)
+            if query_mode == "row":
+                zq = rng.integers(0, n_c, size=(g, Lq))
+            elif query_mode == "tile":
+                zq = np.broadcast_to(z[key_tile_of_query], (g, Lq))
+            else:
+                raise ValueError(f"unknown query_mode {query_mode!r}")
+            qq = r * C[zq] + sigma * rng.standard_normal((g, Lq, D), dtype=np.float32)
+            vv = rng.standard_normal((Lk, Dv), dtype=np.float32)
+            k[b, hk] = _to_tensor(kk, dtype)
+            q[b, hk * g:(hk + 1) * g] = _to_tensor(qq, dtype)
+            v[b, hk] = _to_tensor(vv, dtype)
+    return {"q": q, "k": k, "v": v}
+
+
+def clustered_decode(seed: int, B: int, Hq: int, Hkv: int, Lk: int, D: int, Dv: int,
+                     n_c: int, r: float, latent: bool = False, dtype: str = "bf16",
+                     sigma: float = 0.5, max_hot: int = 3) -> dict:
+    """Tile-clustered single-token decode inputs.
+
+    Draw order: centroids; then for each (b, kv head): tile centroids, key
+    noise, the token's hot-centroid count ``m ~ U{1..max_hot}`` and its ``m``
+    distinct centroids, query noise for the group's heads, then V (skipped
+    when ``latent``: the value rows are then the first ``Dv`` columns of each
+    key row, which the consumer reads out of ``k`` itself).
+
+    Every head of a group shares the token's direction
+    ``u = normalize(sum of its hot centroids)``: ``q_h = r*u + sigma*eps_h``.
+    """
+    rng = np.random.default_rng(seed)
+    g = Hq // Hkv
+    nK = -(-Lk // TILE)
+    C = _centroids(rng, n_c, D)
+    tdt = _torch_dtype(dtype)
+    q = torch.empty((B, Hq, D), dtype=tdt)
+    k = torch.empty((B, Hkv, Lk, D), dtype=tdt)
+    v = None if latent else torch.empty((B, Hkv, Lk, Dv), dtype=tdt)
+    for b in range(B):
+        for hk in range(Hkv):
+            z = rng.integers(0, n_c, size=nK)
+            kz = np.repeat(z, TILE)[:Lk]
+            kk = r * C[kz] + sigma * rng.standard_normal((Lk, D), dtype=np.float32)
+            m = int(rng.integers(1, max_hot + 1))
+            hot = rng.choice(n_c, size=m, replace=False)
+            u = C[hot].sum(axis=0)
+            u /= np.linalg.norm(u)
+            qq = r * u[None, :] + sigma * rng.standard_normal((g, D), dtype=np.float32)
+            k[b, hk] = _to_tensor(kk, dtype)
+            q[b, hk * g:(hk + 1) * g] = _to_tensor(qq, dtype)
+            if not latent:
+                v[b, hk] = _to_tensor(rng.standard_normal((Lk, Dv), dtype=np.float32), dtype)
+    return {"q": q, "k": k, "v": v}
+
+
+def video_dit_field(seed: int, B: int, H: int, grid: tuple = (13, 42, 60), n_field: int = 122,
+                    alpha: float = 4.0, blur: float = 2.0, noise: float = 0.5,
+                    dtype: str = "bf16", heads: int | None = None) -> dict:
+    """Smooth-field self-attention inputs over a (T, H, W) latent grid.
+
+    Tokens are flattened frame-major, then row, then column.  Per (b, head):
+    ``n_field`` channels, each an N(0,1) grid blurred by a Gaussian of ``blur``
+    voxels (reflecting borders) and standardised per channel, give the field
+    ``F``; ``q = F + noise*eps``, ``k = F + noise*eps'``.  Six locality
+    channels ``alpha*[cos(pi*p_a/N_a), sin(pi*p_a/N_a)]`` for each grid axis
+    ``a`` are appended identically to q and k; their dot product is
+    ``alpha^2 * sum_a cos(pi*(p_a - p'_a)/N_a)``, largest for nearby tokens
+    and bounded, so bf16 holds it.  V ~ N(0, 1).  Draw order per (b, head):
+    field grids, query noise, key noise, V.
+
+    ``heads`` generates only the first ``heads`` heads (a bounded sample of
+    the full tensor, bit-identical to its leading heads).
+    """
+    from scipy.ndimage import gaussian_filter
+
+    rng = np.random.default_rng(seed)
+    T, Hh, W = grid
+    L = T * Hh * W
+    D = n_field + 6
+    nh = H if heads is None else heads
+    pt, ph, pw = np.meshgrid(np.arange(T), np.arange(Hh), np.arange(W), indexing="ij")
+    loc = []
+    for p, n in ((pt, T), (ph, Hh), (pw, W)):
+        ang = np.pi * p.reshape(-1).astype(np.float64) / n
+        loc += [np.cos(ang), np.sin(ang)]
+    loc = (alpha * np.stack(loc, axis=1)).astype(np.float32)  # [L, 6]
+    tdt = _torch_dtype(dtype)
+    q = torch.empty((B, nh, L, D), dtype=tdt)
+    k = torch.empty((B, nh, L, D), dtype=tdt)
+    v = torch.empty((B, nh, L, D), dtype=tdt)
+    for b in range(B):
+        for h in range(nh):
+            f = rng.standard_normal((n_field, T, Hh, W), dtype=np.float32)
+            f = gaussian_filter(f, sigma=(0, blur, blur, blur), mode="reflect")
+            f = f.reshape(n_field, L)
+            f = (f - f.mean(axis=1, keepdims=True)) / f.std(axis=1, keepdims=True)
+            F = np.ascontiguousarray(f.T)
+            qf = F + noise * rng.standard_normal((L, n_field), dtype=np.float32)
+            kf = F + noise * rng.standard_normal((L, n_field), dtype=np.float32)
+            q[b, h] = _to_tensor(np.concatenate([qf, loc], axis=1), dtype)
+            k[b, h] = _to_tensor(np.concatenate([kf, loc], axis=1), dtype)
+            v[b, h] = _to_tensor(rng.standard_normal((L, D), dtype=np.float32), dtype)
+    return {"q": q, "k": k, "v": v}

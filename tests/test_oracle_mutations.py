@@ -1,0 +1,89 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each case copies the oracle's source, applies one plausible slip (a flipped
+comparison, a dropped rescale, a wrong head or causal index, ...), loads the
+mutant on the CPU and runs a battery of the pin tests against it.  A mutant
+that passes every pin would mean the pins cannot tell it from the real
+oracle.
+"""
+
+import types
+
+import pytest
+
+import oracle
+import oracle.attention as attention
+from tests import test_oracle_pins as pins  # noqa: E402
+
+EXPORTS = ["decode", "dense_decode", "dense_prefill", "log_threshold", "lse_combine", "n_tiles",
+           "prefill", "skip_fraction", "split_ranges", "stream_pass", "to_f64", "visit_order"]
+
+MUTATIONS = {
+    "non-strict comparison": ("skip = np.full(rows, delta < ln_thr)",
+                              "skip = np.full(rows, delta <= ln_thr)"),
+    "skipped tile leaves m alone": ("            m = m_new\n",
+                                    "            m = np.where(keep, m_new, m)\n"),
+    "top-left causal alignment": ("rows[:, None] + (Lk - Lq)] = NEG_INF",
+                                  "rows[:, None]] = NEG_INF"),
+    "kv head h % Hkv": ("hk = h // g\n", "hk = h % Hkv\n"),
+    "no rescale of l": ("l = alpha * l + ", "l = l + "),
+    "no rescale of O": ("O = alpha[:, None] * O + ", "O = O + "),
+    "skipped tile still adds to l": ("np.where(keep, p.sum(axis=1), 0.0)", "p.sum(axis=1)"),
+    "delta sign flipped": ("tile_max - m))", "m - tile_max))"),
+    "uniform takes min over rows": ("delta = float(delta_r.max())", "delta = float(delta_r.min())"),
+    "first visible tile may be skipped": ("np.where(m == NEG_INF, math.inf, tile_max - m)",
+                                          "np.where(m == NEG_INF, NEG_INF, tile_max - m)"),
+    "floor split size": ("per = -(-nK // S)", "per = max(1, nK // S)"),
+    "lse combine ignores weights": ("wn = np.where(fin[None, :], w / np.where(fin, tot, 1.0)[None, :], 0.0)",
+                                    "wn = np.full_like(w, 1.0 / w.shape[0])"),
+    "diag_first causal ascending": ("            return tiles[::-1]", "            return tiles"),
+    "wrong tile of a key": ("keys = np.arange(j * tk, min((j + 1) * tk, Lk))",
+                            "keys = np.arange(j * tk, min((j + 1) * tk + 1, Lk))"),
+    "natural-log threshold replaced by log10": ("math.log(thr)", "math.log10(thr)"),
+}
+
+
+def mutant(old, new):
+    with open(attention.__file__) as f:
+        src = f.read()
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def battery():
+    yield lambda: [pins.test_hand_worked_example(c) for c in range(10)]
+    yield pins.test_ties_are_kept
+    yield lambda: pins.test_threshold_zero_is_softmax_attention_prefill(True, "ascending",
+                                                                        (200, 333, 128, 128))
+    yield lambda: pins.test_threshold_zero_is_softmax_attention_prefill(False, "diag_first",
+                                                                        (333, 200, 64, 32))
+    yield lambda: pins.test_threshold_zero_is_softmax_attention_decode(3, False)
+    yield lambda: pins.test_threshold_at_least_one_keeps_only_record_tiles(1.0, "diag_first", True)
+    yield lambda: pins.test_threshold_at_least_one_keeps_only_record_tiles(2.5, "ascending", False)
+    yield lambda: [pins.test_brute_force_mask_enumeration(s, t, 4) for s in range(3)
+                   for t in (0.05, 1.0, 3.0)]
+    yield lambda: pins.test_brute_force_per_row_and_splits(0, 0.5)
+    yield pins.test_visit_orders
+    yield pins.test_split_ranges
+    yield pins.test_uniform_skips_only_where_every_row_skips
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    mod = mutant(*MUTATIONS[name])
+    for e in EXPORTS:
+        monkeypatch.setattr(oracle, e, getattr(mod, e))
+    caught = []
+    for check in battery():
+        try:
+            check()
+        except AssertionError:
+            caught.append(check)
+    assert caught, f"no pin caught the planted mistake: {name}"
+
+
+def test_unmutated_battery_passes():
+    for check in battery():
+        check()
