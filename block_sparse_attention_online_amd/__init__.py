@@ -1,0 +1,333 @@
+"""Skip-softmax (BLASST) attention for AMD MI355X: Python binding of libssattn.so.
+
+The functions here carry the C entry points' names (include/ss_attn.h) and do
+argument marshalling only: they check device, dtype, contiguity and shapes of
+torch tensors, allocate outputs when asked to, and pass raw device pointers
+and the current HIP stream to the library.  Every step of the attention runs
+in the library's gfx950 kernels; there is no CPU or PyTorch fallback, and
+importing a function that needs the library raises if it was not built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "ss_attn_prefill", "ss_attn_prefill_f32", "ss_attn_prefill_ex", "ss_attn_decode",
+    "ss_attn_decode_partial", "ss_attn_decode_combine",
+    "ss_attn_decode_workspace_bytes", "ss_decode_num_splits", "ss_factor", "ss_threshold",
+    "ss_gate_enabled", "ss_resolve_threshold", "ss_last_error", "ss_version", "library_path",
+    "SSError", "TILE", "ORDERS", "mask_shape_prefill", "mask_shape_decode",
+]
+
+TILE = 128
+ORDERS = {"ascending": 0, "diag_first": 1}
+SS_FACTOR_DIRECT, SS_FACTOR_CALIBRATED = 0, 1
+_DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libssattn.so")
+
+
+class SSError(RuntimeError):
+    """A non-zero ss_status from the library."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"ssattn error {code}: {msg}")
+        self.code = code
+
+
+class _PrefillParams(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("B", ctypes.c_int), ("Hq", ctypes.c_int),
+                ("Hkv", ctypes.c_int), ("Lq", ctypes.c_int), ("Lk", ctypes.c_int),
+                ("D", ctypes.c_int), ("Dv", ctypes.c_int), ("scale", ctypes.c_float),
+                ("threshold", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("order", ctypes.c_int), ("skip_mask_out", ctypes.c_void_p)]
+
+
+_LIB = None
+
+_P, _I, _F, _D, _SZ, _I64 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double,
+                             ctypes.c_size_t, ctypes.c_int64)
+_SIGNATURES = {
+    "ss_attn_prefill": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _F, _P, _P]),
+    "ss_attn_prefill_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _F, _P, _P]),
+    "ss_attn_prefill_ex": (_I, [ctypes.POINTER(_PrefillParams), _P]),
+    "ss_attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _P, _SZ, _P]),
+    "ss_attn_decode_partial": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _P, _SZ,
+                                    _P]),
+    "ss_attn_decode_combine": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "ss_attn_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "ss_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
+    "ss_factor": (_I, [_I, _D, _D, _D, _D, _I64, ctypes.POINTER(_D)]),
+    "ss_threshold": (_I, [_D, _I64, ctypes.POINTER(_D)]),
+    "ss_gate_enabled": (_I, [_I, _D, _I, _D]),
+    "ss_resolve_threshold": (_I, [_I, _D, _D, _D, _D, _I64, _I, _D, _I, _D,
+                                  ctypes.POINTER(_F)]),
+    "ss_last_error": (ctypes.c_char_p, []),
+    "ss_version": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libssattn.so (built in-tree by build.py); raise if it is missing."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m block_sparse_attention_online_amd.build`")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def ss_last_error() -> str:
+    return lib().ss_last_error().decode()
+
+
+def ss_version() -> str:
+    return lib().ss_version().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise SSError(rc, ss_last_error())
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t.data_ptr()
+
+
+def mask_shape_prefill(B, Hq, Lq, Lk):
+    return (B, Hq, -(-Lq // TILE), -(-Lk // TILE))
+
+
+def mask_shape_decode(B, Hkv, Lk):
+    return (B, Hkv, -(-Lk // TILE))
+
+
+# --------------------------------------------------------------------------- prefill
+
+def ss_attn_prefill_ex(q, k, v, out=None, *, scale=None, causal=False, threshold=0.0,
+                       skip_mask=None, order="ascending", stream=None):
+    """Skip-softmax prefill: q[B,Hq,Lq,D], k[B,Hkv,Lk,D], v[B,Hkv,Lk,Dv] on the GPU
+    (all bf16 or all fp32).  Returns ``out`` [B,Hq,Lq,Dv]; fills ``skip_mask``
+    (u8 [B,Hq,ceil(Lq/128),ceil(Lk/128)]) when given.  Asynchronous on
+    ``stream`` (default: the current stream)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, L, D]")
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lk, Dk = k.shape
+    if (Bk, Dk) != (B, D) or tuple(v.shape[:3]) != (B, Hkv, Lk):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    Dv = v.shape[3]
+    if q.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dt = q.dtype
+    if out is None:
+        out = torch.empty((B, Hq, Lq, Dv), dtype=dt, device=q.device)
+    elif tuple(out.shape) != (B, Hq, Lq, Dv):
+        raise ValueError(f"out must be {(B, Hq, Lq, Dv)}")
+    mptr = None
+    if skip_mask is not None:
+        if tuple(skip_mask.shape) != mask_shape_prefill(B, Hq, Lq, Lk):
+            raise ValueError(f"skip_mask must be {mask_shape_prefill(B, Hq, Lq, Lk)}")
+        mptr = _dev(skip_mask, "skip_mask", torch.uint8)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if order not in ORDERS:
+        raise ValueError(f"order must be one of {sorted(ORDERS)}")
+    p = _PrefillParams(_dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _dev(out, "out", dt),
+                       B, Hq, Hkv, Lq, Lk, D, Dv, float(scale), float(threshold), int(bool(causal)),
+                       _DTYPE[dt], ORDERS[order], mptr)
+    _check(lib().ss_attn_prefill_ex(ctypes.byref(p), _stream(stream, q.device)))
+    return out
+
+
+def ss_attn_prefill(q, k, v, out=None, *, scale=None, causal=False, threshold=0.0,
+                    skip_mask=None, stream=None):
+    """bf16 skip-softmax prefill in ascending key-tile order (see ss_attn_prefill_ex)."""
+    if q.dtype != torch.bfloat16:
+        raise TypeError("ss_attn_prefill takes bf16 tensors")
+    return ss_attn_prefill_ex(q, k, v, out, scale=scale, causal=causal, threshold=threshold,
+                              skip_mask=skip_mask, stream=stream)
+
+
+def ss_attn_prefill_f32(q, k, v, out=None, *, scale=None, causal=False, threshold=0.0,
+                        skip_mask=None, stream=None):
+    """fp32 debug path of the skip-softmax prefill (see ss_attn_prefill_ex)."""
+    if q.dtype != torch.float32:
+        raise TypeError("ss_attn_prefill_f32 takes fp32 tensors")
+    return ss_attn_prefill_ex(q, k, v, out, scale=scale, causal=causal, threshold=threshold,
+                              skip_mask=skip_mask, stream=stream)
+
+
+# --------------------------------------------------------------------------- decode
+
+def ss_decode_num_splits(B, Hq, Hkv, Lk, D, Dv) -> int:
+    return int(lib().ss_decode_num_splits(B, Hq, Hkv, Lk, D, Dv))
+
+
+def ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits=0) -> int:
+    return int(lib().ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits))
+
+
+def _decode_args(q, k, v, dv, skip_mask, workspace, num_splits, scale):
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and k [B, Hkv, Lk, D]")
+    B, Hq, D = q.shape
+    Bk, Hkv, Lk, Dk = k.shape
+    if (Bk, Dk) != (B, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)}")
+    dt = torch.bfloat16
+    if v is None:
+        if dv is None:
+            raise ValueError("v=None needs dv (value columns of the latent row)")
+        Dv, vptr = int(dv), None
+    else:
+        if v.dim() != 4 or tuple(v.shape[:3]) != (B, Hkv, Lk):
+            raise ValueError(f"v must be [B, Hkv, Lk, Dv] (got {tuple(v.shape)})")
+        Dv, vptr = v.shape[3], _dev(v, "v", dt)
+    mptr = None
+    if skip_mask is not None:
+        if tuple(skip_mask.shape) != mask_shape_decode(B, Hkv, Lk):
+            raise ValueError(f"skip_mask must be {mask_shape_decode(B, Hkv, Lk)}")
+        mptr = _dev(skip_mask, "skip_mask", torch.uint8)
+    need = ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return dict(B=B, Hq=Hq, Hkv=Hkv, Lk=Lk, D=D, Dv=Dv, vptr=vptr, mptr=mptr,
+                workspace=workspace, scale=float(scale),
+                qptr=_dev(q, "q", dt), kptr=_dev(k, "k", dt))
+
+
+def ss_attn_decode_partial(q, k, v=None, *, dv=None, scale=None, threshold=0.0, num_splits=0,
+                           skip_mask=None, workspace=None, stream=None):
+    """First stage of ss_attn_decode: run every split into ``workspace`` (returned)."""
+    a = _decode_args(q, k, v, dv, skip_mask, workspace, num_splits, scale)
+    ws = a["workspace"]
+    _check(lib().ss_attn_decode_partial(a["qptr"], a["kptr"], a["vptr"], a["B"], a["Hq"], a["Hkv"],
+                                        a["Lk"], a["D"], a["Dv"], a["scale"], float(threshold),
+                                        int(num_splits), a["mptr"], _dev(ws, "workspace"),
+                                        ws.numel() * ws.element_size(), _stream(stream, q.device)))
+    return ws
+
+
+def ss_attn_decode_combine(workspace, out, *, B, Hq, Hkv, Lk, D, Dv, num_splits=0, stream=None):
+    """Second stage of ss_attn_decode: log-sum-exp merge of the split partials into ``out``."""
+    _check(lib().ss_attn_decode_combine(_dev(out, "out", torch.bfloat16), B, Hq, Hkv, Lk, D, Dv,
+                                        int(num_splits), _dev(workspace, "workspace"),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream, out.device)))
+    return out
+
+
+def ss_attn_decode(q, k, v=None, out=None, *, dv=None, scale=None, threshold=0.0, num_splits=0,
+                   skip_mask=None, workspace=None, stream=None):
+    """Split-KV skip-softmax decode: q[B,Hq,D], k[B,Hkv,Lk,D], v[B,Hkv,Lk,Dv] bf16,
+    or ``v=None`` with ``dv`` for a latent cache whose value rows are the first
+    ``dv`` columns of each key row.  Returns ``out`` [B,Hq,Dv]; fills
+    ``skip_mask`` (u8 [B,Hkv,ceil(Lk/128)]) when given.  ``workspace``: a
+    uint8 GPU tensor of at least ss_attn_decode_workspace_bytes() bytes
+    (allocated here when None)."""
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and k [B, Hkv, Lk, D]")
+    B, Hq, D = q.shape
+    Bk, Hkv, Lk, Dk = k.shape
+    if (Bk, Dk) != (B, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)}")
+    dt = torch.bfloat16
+    if v is None:
+        if dv is None:
+            raise ValueError("v=None needs dv (value columns of the latent row)")
+        Dv, vptr = int(dv), None
+    else:
+        if v.dim() != 4 or tuple(v.shape[:3]) != (B, Hkv, Lk):
+            raise ValueError(f"v must be [B, Hkv, Lk, Dv] (got {tuple(v.shape)})")
+        Dv, vptr = v.shape[3], _dev(v, "v", dt)
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=dt, device=q.device)
+    elif tuple(out.shape) != (B, Hq, Dv):
+        raise ValueError(f"out must be {(B, Hq, Dv)}")
+    mptr = None
+    if skip_mask is not None:
+        if tuple(skip_mask.shape) != mask_shape_decode(B, Hkv, Lk):
+            raise ValueError(f"skip_mask must be {mask_shape_decode(B, Hkv, Lk)}")
+        mptr = _dev(skip_mask, "skip_mask", torch.uint8)
+    need = ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = lib().ss_attn_decode(_dev(q, "q", dt), _dev(k, "k", dt), vptr, _dev(out, "out", dt), B,
+                              Hq, Hkv, Lk, D, Dv, float(scale), float(threshold), int(num_splits),
+                              mptr, _dev(workspace, "workspace"), wbytes,
+                              _stream(stream, q.device))
+    _check(rc)
+    return out
+
+
+# --------------------------------------------------------------------------- host helpers
+
+def ss_factor(mode, a=0.0, b=0.0, target_sparsity=0.0, threshold=0.0, seqlen=1) -> float:
+    """Calibrated factor a*exp(b*target_sparsity) or direct factor threshold*seqlen."""
+    m = {"direct": SS_FACTOR_DIRECT, "calibrated": SS_FACTOR_CALIBRATED}.get(mode, mode)
+    out = ctypes.c_double()
+    _check(lib().ss_factor(int(m), a, b, target_sparsity, threshold, int(seqlen),
+                           ctypes.byref(out)))
+    return out.value
+
+
+def ss_threshold(factor, seqlen) -> float:
+    out = ctypes.c_double()
+    _check(lib().ss_threshold(float(factor), int(seqlen), ctypes.byref(out)))
+    return out.value
+
+
+def ss_gate_enabled(timestep=None, disabled_until=None) -> bool:
+    return bool(lib().ss_gate_enabled(timestep is not None, 0.0 if timestep is None else timestep,
+                                      disabled_until is not None,
+                                      0.0 if disabled_until is None else disabled_until))
+
+
+def ss_resolve_threshold(mode, *, a=0.0, b=0.0, target_sparsity=0.0, threshold=0.0, seqlen=1,
+                         timestep=None, disabled_until=None) -> float:
+    """The fp32 threshold a kernel call receives: 0 (dense) when gated off."""
+    m = {"direct": SS_FACTOR_DIRECT, "calibrated": SS_FACTOR_CALIBRATED}.get(mode, mode)
+    out = ctypes.c_float()
+    _check(lib().ss_resolve_threshold(int(m), a, b, target_sparsity, threshold, int(seqlen),
+                                      timestep is not None, 0.0 if timestep is None else timestep,
+                                      disabled_until is not None,
+                                      0.0 if disabled_until is None else disabled_until,
+                                      ctypes.byref(out)))
+    return out.value

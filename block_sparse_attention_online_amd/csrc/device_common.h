@@ -1,0 +1,137 @@
+// Device helpers shared by the gfx950 kernels: vector types for the bf16 MFMA
+// operands, bf16 packing, wave reductions, and the key-tile visit order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssattn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kTile = 128;  // keys per tile, query rows per prefill decision block
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+__device__ __forceinline__ float pos_inf() { return __builtin_inff(); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) {
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 values -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  bf16x2_t r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(unsigned int, r);
+}
+
+// 2^x on the hardware exponential unit.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- cross-lane helpers -------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;         // row_ror:4
+constexpr int kDppRor8 = 0x128;         // row_ror:8
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
+
+// Sum over each aligned group of N lanes (N = 8 or 16); every lane of the
+// group receives the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group size");
+  if constexpr (N == 16) {
+    x += dpp<kDppRor8>(x);
+    x += dpp<kDppRor4>(x);
+  } else {
+    x += dpp<kDppHalfMirror>(x);
+  }
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppXor1>(x);
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Max over lanes whose index differs only in bits [lo_bit, 6).
+template <int LO>
+__device__ __forceinline__ float lanes_max_from(float x) {
+#pragma unroll
+  for (int m = 32; m >= LO; m >>= 1) x = fmaxf(x, shfl_xor_f(x, m));
+  return x;
+}
+template <int LO>
+__device__ __forceinline__ float lanes_sum_from(float x) {
+#pragma unroll
+  for (int m = 32; m >= LO; m >>= 1) x += shfl_xor_f(x, m);
+  return x;
+}
+
+// ---- key-tile visit order ---------------------------------------------------------
+
+// Tiles visited by one query tile of a prefill call: `count` tiles starting at
+// `first`; the t-th visited tile is tile_at(t).  Causal keeps only tiles with
+// a key visible to some row (key c visible to row r iff c <= r + Lk - Lq).
+struct VisitPlan {
+  int count;  // number of visited tiles
+  int last;   // causal: highest visited tile
+  int start;  // non-causal diag_first: first tile
+  int nK;
+  int causal;
+  int diag_first;
+
+  __device__ __forceinline__ int tile_at(int t) const {
+    if (causal) return diag_first ? last - t : t;
+    if (diag_first) {
+      int j = start + t;
+      return j >= nK ? j - nK : j;
+    }
+    return t;
+  }
+};
+
+__device__ __forceinline__ VisitPlan make_visit_plan(int qtile, int Lq, int Lk, int causal,
+                                                     int diag_first) {
+  VisitPlan p;
+  p.nK = (Lk + kTile - 1) / kTile;
+  p.causal = causal;
+  p.diag_first = diag_first;
+  const int r0 = qtile * kTile;
+  const int r1 = min(r0 + kTile, Lq) - 1;
+  if (causal) {
+    const long last_key = (long)r1 + Lk - Lq;
+    if (last_key < 0) {
+      p.count = 0;
+      p.last = -1;
+    } else {
+      p.last = min(p.nK - 1, (int)(last_key / kTile));
+      p.count = p.last + 1;
+    }
+    p.start = 0;
+  } else {
+    p.count = p.nK;
+    p.last = p.nK - 1;
+    long s = ((long)r0 + Lk - Lq) / kTile;
+    if ((long)r0 + Lk - Lq < 0) s = 0;
+    p.start = (int)min((long)(p.nK - 1), s);
+  }
+  return p;
+}
+
+}  // namespace ssattn

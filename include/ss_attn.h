@@ -1,0 +1,222 @@
+/*
+ * ss_attn.h -- C ABI of the skip-softmax (BLASST) attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method.  Attention is computed in one streaming online-softmax pass
+ * over key tiles of 128 keys.  Per query row the pass keeps the running max m,
+ * the running denominator l = sum exp(s - m) and the running numerator
+ * O = sum exp(s - m) v, rescaling l and O when m grows, and returns O / l
+ * (vLLM-Omni design page "Skip-Softmax", section "The online-softmax pass").
+ * Each tile's scores S = Q K_j^T * scale are always computed; the tile is then
+ * skipped -- no exponentials, no P.V accumulation, and in decode no V read --
+ * when exp(tile_max - running_max) < threshold (same page, "The skip test";
+ * BLASST summary page of arXiv 2512.12087, sections "Kerninzicht" and
+ * "Kernel-ontwerp").  The threshold is normalised by the sequence length,
+ * threshold = factor / seqlen, with a calibrated or a direct factor (design
+ * page, "The threshold"), and the mode can be gated off during early
+ * diffusion timesteps (design page, "Timestep gating").
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are dense, contiguous, head-major device buffers owned by the
+ *    caller; the library allocates no device memory and keeps no state other
+ *    than a thread-local error string.
+ *  - Kernels are enqueued on `stream` and the call returns without
+ *    synchronising.  A NULL stream is the default stream.
+ *  - A tile is skipped iff  max over the rows of its decision block of
+ *    (tile_max_r - m_r)  <  ln(threshold), where m_r is the running max of
+ *    row r before the tile.  A row that has seen no key yet never lets its
+ *    first visible tile be skipped; a row that sees no key of the tile does
+ *    not hold the tile.  The comparison is strict, so threshold 0 is exactly
+ *    dense attention.  A skipped tile still updates m (its scores were
+ *    computed); when threshold > 1 lets a skipped tile raise m, l and O are
+ *    rescaled so the result stays exact over the kept keys.
+ *  - Skip-mask bytes: 0 = tile computed, 1 = tile skipped, 2 = tile not
+ *    visited (entirely above the causal diagonal).
+ *  - Every function returns an ss_status.  On failure nothing is launched and
+ *    ss_last_error() describes the problem.
+ */
+#ifndef SS_ATTN_H
+#define SS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_TILE_KEYS 128 /* keys per tile (design page, "The online-softmax pass") */
+#define SS_TILE_ROWS 128 /* query rows per prefill decision block */
+
+typedef enum {
+  SS_OK = 0,
+  SS_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad threshold, Hq % Hkv != 0 */
+  SS_ERR_UNSUPPORTED = -2, /* head dimensions or grouping without a kernel */
+  SS_ERR_HIP = -3,         /* a HIP launch failed; see ss_last_error() */
+  SS_ERR_WORKSPACE = -4    /* decode workspace missing or too small */
+} ss_status;
+
+typedef enum { SS_FACTOR_DIRECT = 0, SS_FACTOR_CALIBRATED = 1 } ss_factor_mode;
+typedef enum { SS_DTYPE_BF16 = 0, SS_DTYPE_F32 = 1 } ss_dtype;
+
+/* Key-tile visit order of a prefill query tile.  ASCENDING walks tiles
+ * 0, 1, ...  DIAG_FIRST starts at the query tile's diagonal: causal goes from
+ * the last visible tile down to tile 0; non-causal goes from the query tile's
+ * own key tile upwards and wraps to tile 0.  The pages describe a single
+ * streaming pass and do not fix the order. */
+typedef enum { SS_ORDER_ASCENDING = 0, SS_ORDER_DIAG_FIRST = 1 } ss_order;
+
+enum { SS_MASK_COMPUTED = 0, SS_MASK_SKIPPED = 1, SS_MASK_UNVISITED = 2 };
+
+/* ------------------------------------------------------------------ prefill */
+
+/*
+ * Skip-softmax prefill (design page, "The online-softmax pass" and "The skip
+ * test"; BLASST summary, "Kernel-ontwerp": the prefill kernel skips the
+ * exponentials and the P.V matrix multiply of skipped tiles).
+ *
+ *   q   [B, Hq,  Lq, D ]  bf16     k [B, Hkv, Lk, D]  bf16
+ *   v   [B, Hkv, Lk, Dv]  bf16   out [B, Hq,  Lq, Dv] bf16 (written)
+ *   skip_mask_out  u8 [B, Hq, ceil(Lq/128), ceil(Lk/128)] or NULL (written)
+ *
+ * Query head h reads KV head h / (Hq / Hkv).  The skip decision for key tile
+ * j is uniform over each 128-row query tile of one head.  `causal` masks key
+ * c from query row r when c > r + Lk - Lq (bottom-right alignment); rows that
+ * see no key produce 0.  Supported: D == Dv in {64, 128}.  `scale` > 0 and
+ * finite; `threshold` finite and >= 0.  Key tiles are visited in ascending
+ * order.
+ */
+int ss_attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int Hq,
+                    int Hkv, int Lq, int Lk, int D, int Dv, float scale, int causal,
+                    float threshold, uint8_t* skip_mask_out, hipStream_t stream);
+
+/* fp32 debug path: the same operation and arguments with fp32 q, k, v, out,
+ * computed in fp32 throughout (no bf16 rounding of P). */
+int ss_attn_prefill_f32(const float* q, const float* k, const float* v, float* out, int B,
+                        int Hq, int Hkv, int Lq, int Lk, int D, int Dv, float scale, int causal,
+                        float threshold, uint8_t* skip_mask_out, hipStream_t stream);
+
+/* Full form: the two calls above are this one with dtype BF16 / F32 and
+ * order ASCENDING. */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int B, Hq, Hkv, Lq, Lk, D, Dv;
+  float scale;
+  float threshold;
+  int causal;
+  int dtype; /* ss_dtype */
+  int order; /* ss_order */
+  uint8_t* skip_mask_out;
+} ss_prefill_params;
+
+int ss_attn_prefill_ex(const ss_prefill_params* p, hipStream_t stream);
+
+/* ------------------------------------------------------------------ decode */
+
+/*
+ * Split-KV skip-softmax decode of one query token per sequence (BLASST
+ * summary, "Kerninzicht" and "Kernel-ontwerp": in decode a skipped tile also
+ * skips its V load from HBM, and V loads of surviving tiles are issued
+ * together).
+ *
+ *   q   [B, Hq, D]  bf16           k [B, Hkv, Lk, D] bf16
+ *   v   [B, Hkv, Lk, Dv] bf16, or NULL: the value row of key c is then the
+ *       first Dv columns of key row c (a shared latent cache, Dv <= D)
+ *   out [B, Hq, Dv] bf16 (written)
+ *   skip_mask_out  u8 [B, Hkv, ceil(Lk/128)] or NULL (written)
+ *
+ * The key tiles are cut into num_splits contiguous splits of
+ * ceil(nK / num_splits) tiles each (the last may be shorter; num_splits is
+ * clamped to [1, nK] and empty trailing splits are dropped).  Each split is an
+ * independent streaming pass with its own running max; a second kernel merges
+ * the splits with a log-sum-exp combine.  The skip decision is uniform over
+ * the Hq/Hkv query heads that share a KV head.  num_splits = 0 selects
+ * ss_decode_num_splits().
+ *
+ * `workspace` is caller-owned device memory of at least
+ * ss_attn_decode_workspace_bytes() bytes (split partials); its contents on
+ * entry do not matter.  Supported: (D, Dv) = (64, 64) or (128, 128) with
+ * Hq/Hkv in {1, 2, 4, 8}; (576, 512) with v == NULL and Hq/Hkv a multiple of
+ * 16 up to 128.
+ */
+int ss_attn_decode(const void* q, const void* k, const void* v, void* out, int B, int Hq,
+                   int Hkv, int Lk, int D, int Dv, float scale, float threshold, int num_splits,
+                   uint8_t* skip_mask_out, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/* The two stages of ss_attn_decode, for callers that time or schedule them
+ * separately (or merge partials produced elsewhere).  ss_attn_decode_partial
+ * runs every split (same arguments as ss_attn_decode minus `out`) and leaves
+ * the split results in `workspace`: O_s / l_s as fp32 [S][B][Hq][Dv], then,
+ * at the next 256-byte boundary, lse_s = m_s + ln l_s as fp32 [S][B][Hq],
+ * with S the effective split count.  ss_attn_decode_combine merges them into
+ * `out` with the log-sum-exp rule; `num_splits` and the sizes must be those
+ * of the partial call. */
+int ss_attn_decode_partial(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                           int Lk, int D, int Dv, float scale, float threshold, int num_splits,
+                           uint8_t* skip_mask_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+int ss_attn_decode_combine(void* out, int B, int Hq, int Hkv, int Lk, int D, int Dv,
+                           int num_splits, const void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Bytes of decode workspace for these sizes (num_splits as for
+ * ss_attn_decode, 0 = automatic).  Returns 0 for invalid sizes. */
+size_t ss_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lk, int D, int Dv,
+                                      int num_splits);
+
+/* The automatic split count: deterministic in the sizes, exported so that a
+ * reference can reproduce the same partition.  Returns a value in [1, nK], or
+ * 0 for invalid sizes. */
+int ss_decode_num_splits(int B, int Hq, int Hkv, int Lk, int D, int Dv);
+
+/* ------------------------------------------------------------------ host helpers */
+
+/*
+ * factor of the per-tile threshold (design page, "The threshold"):
+ *   SS_FACTOR_CALIBRATED: factor = a * exp(b * target_sparsity), with a, b
+ *                         fitted per model; target_sparsity in [0, 1].
+ *   SS_FACTOR_DIRECT:     factor = threshold * seqlen (calibration free).
+ * Rejects seqlen <= 0 and non-finite inputs.  Writes *factor_out.
+ */
+int ss_factor(ss_factor_mode mode, double a, double b, double target_sparsity,
+              double threshold, int64_t seqlen, double* factor_out);
+
+/* threshold = factor / seqlen (design page, "The threshold"; BLASST summary,
+ * "Calibratie en Thresholding": inversely proportional to the context
+ * length).  Rejects seqlen <= 0 and a negative or non-finite factor. */
+int ss_threshold(double factor, int64_t seqlen, double* threshold_out);
+
+/*
+ * Timestep gating (design page, "Timestep gating"): returns 1 (sparse) or 0
+ * (dense).  Without disabled_until the mode is always on; with it, the mode
+ * is on once a published timestep t satisfies t <= disabled_until, and a
+ * pipeline that publishes no timestep stays dense.
+ */
+int ss_gate_enabled(int has_timestep, double t, int has_disabled_until, double disabled_until);
+
+/*
+ * The kernel threshold for one call: dense (0) when the gate is off;
+ * otherwise the direct user threshold unchanged (no factor round trip), or
+ * factor / seqlen with the calibrated factor.  Writes *threshold_out.
+ */
+int ss_resolve_threshold(ss_factor_mode mode, double a, double b, double target_sparsity,
+                         double threshold, int64_t seqlen, int has_timestep, double t,
+                         int has_disabled_until, double disabled_until, float* threshold_out);
+
+/* Thread-local description of the last failure ("" if none). */
+const char* ss_last_error(void);
+
+/* Library version string. */
+const char* ss_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_ATTN_H */

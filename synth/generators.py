@@ -1,7 +1,10 @@
 """Seeded generators for attention inputs with block-structured score mass.
 
-Every generator uses ``numpy.random.default_rng(seed)`` (PCG64) and draws in a
-fixed order so a seed names one exact tensor set.  Values are drawn in fp32 and,
+Every generator uses numpy's PCG64 streams and draws in a fixed order, so a
+seed names one exact tensor set: shared draws (the centroids) come from
+``default_rng(seed)``, and each (batch, head) unit draws from its own stream
+``default_rng([seed, b, h])``, which lets units be generated in parallel
+threads without changing any value.  Values are drawn in fp32 and,
 for bf16 workloads, rounded once to bf16 with round-to-nearest-even (torch's
 CPU cast).  Whatever consumes the tensors (the fp64 oracle, the GPU kernels)
 reads back exactly those rounded values.
@@ -20,10 +23,30 @@ Two families:
 
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import torch
 
 TILE = 128  # keys per tile that a centroid is assigned to
+
+
+def _unit_rng(seed: int, *unit: int) -> np.random.Generator:
+    return np.random.default_rng([seed, *unit])
+
+
+def _for_units(units, fn) -> None:
+    """Run fn(unit) over all units on a small thread pool (numpy and torch
+    release the GIL in the bulk fills and casts)."""
+    units = list(units)
+    n = min(len(units), max(1, min(16, os.cpu_count() or 1)))
+    if n <= 1:
+        for u in units:
+            fn(u)
+        return
+    with cf.ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(fn, units))
 
 
 def bf16_round(x: np.ndarray) -> torch.Tensor:
@@ -54,10 +77,11 @@ def clustered_prefill(seed: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, D:
                       sigma: float = 0.5) -> dict:
     """Tile-clustered Q/K/V for a prefill call.
 
-    Draw order: centroids ``C`` (n_c x D, row-normalised); then for each
-    (b, kv head) in order: tile centroids ``z`` (one per 128-key tile), key
-    noise, query centroid choices (``query_mode == "row"`` only), query noise
-    for the ``Hq/Hkv`` heads of the group, then V ~ N(0, 1).
+    Draw order: centroids ``C`` (n_c x D, row-normalised) from the shared
+    stream; then, from the stream of each (b, kv head): tile centroids ``z``
+    (one per 128-key tile), key noise, query centroid choices
+    (``query_mode == "row"`` only), query noise for the ``Hq/Hkv`` heads of
+    the group, then V ~ N(0, 1).
 
     ``k = r*C[z_tile] + sigma*eps``.  Queries:
 
@@ -76,22 +100,26 @@ def clustered_prefill(seed: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, D:
     k = torch.empty((B, Hkv, Lk, D), dtype=tdt)
     v = torch.empty((B, Hkv, Lk, Dv), dtype=tdt)
     key_tile_of_query = np.clip(np.arange(Lq) + (Lk - Lq), 0, Lk - 1) // TILE
-    for b in range(B):
-        for hk in range(Hkv):
-            z = rng.integers(0, n_c, size=nK)
-            kz = np.repeat(z, TILE)[:Lk]
-            kk = r * C[kz] + sigma * rng.standard_normal((Lk, D), dtype=np.float32)
-            if query_mode == "row":
-                zq = rng.integers(0, n_c, size=(g, Lq))
-            elif query_mode == "tile":
-                zq = np.broadcast_to(z[key_tile_of_query], (g, Lq))
-            else:
-                raise ValueError(f"unknown query_mode {query_mode!r}")
-            qq = r * C[zq] + sigma * rng.standard_normal((g, Lq, D), dtype=np.float32)
-            vv = rng.standard_normal((Lk, Dv), dtype=np.float32)
-            k[b, hk] = _to_tensor(kk, dtype)
-            q[b, hk * g:(hk + 1) * g] = _to_tensor(qq, dtype)
-            v[b, hk] = _to_tensor(vv, dtype)
+
+    def unit(bh):
+        b, hk = bh
+        rng = _unit_rng(seed, b, hk)
+        z = rng.integers(0, n_c, size=nK)
+        kz = np.repeat(z, TILE)[:Lk]
+        kk = r * C[kz] + sigma * rng.standard_normal((Lk, D), dtype=np.float32)
+        if query_mode == "row":
+            zq = rng.integers(0, n_c, size=(g, Lq))
+        elif query_mode == "tile":
+            zq = np.broadcast_to(z[key_tile_of_query], (g, Lq))
+        else:
+            raise ValueError(f"unknown query_mode {query_mode!r}")
+        qq = r * C[zq] + sigma * rng.standard_normal((g, Lq, D), dtype=np.float32)
+        vv = rng.standard_normal((Lk, Dv), dtype=np.float32)
+        k[b, hk] = _to_tensor(kk, dtype)
+        q[b, hk * g:(hk + 1) * g] = _to_tensor(qq, dtype)
+        v[b, hk] = _to_tensor(vv, dtype)
+
+    _for_units([(b, hk) for b in range(B) for hk in range(Hkv)], unit)
     return {"q": q, "k": k, "v": v}
 
 
@@ -100,9 +128,9 @@ def clustered_decode(seed: int, B: int, Hq: int, Hkv: int, Lk: int, D: int, Dv: 
                      sigma: float = 0.5, max_hot: int = 3) -> dict:
     """Tile-clustered single-token decode inputs.
 
-    Draw order: centroids; then for each (b, kv head): tile centroids, key
-    noise, the token's hot-centroid count ``m ~ U{1..max_hot}`` and its ``m``
-    distinct centroids, query noise for the group's heads, then V (skipped
+    Draw order: centroids from the shared stream; then, from the stream of
+    each (b, kv head): tile centroids, key noise, the token's hot-centroid
+    count ``m ~ U{1..max_hot}`` and its ``m`` distinct centroids, query noise for the group's heads, then V (skipped
     when ``latent``: the value rows are then the first ``Dv`` columns of each
     key row, which the consumer reads out of ``k`` itself).
 
@@ -117,20 +145,24 @@ def clustered_decode(seed: int, B: int, Hq: int, Hkv: int, Lk: int, D: int, Dv: 
     q = torch.empty((B, Hq, D), dtype=tdt)
     k = torch.empty((B, Hkv, Lk, D), dtype=tdt)
     v = None if latent else torch.empty((B, Hkv, Lk, Dv), dtype=tdt)
-    for b in range(B):
-        for hk in range(Hkv):
-            z = rng.integers(0, n_c, size=nK)
-            kz = np.repeat(z, TILE)[:Lk]
-            kk = r * C[kz] + sigma * rng.standard_normal((Lk, D), dtype=np.float32)
-            m = int(rng.integers(1, max_hot + 1))
-            hot = rng.choice(n_c, size=m, replace=False)
-            u = C[hot].sum(axis=0)
-            u /= np.linalg.norm(u)
-            qq = r * u[None, :] + sigma * rng.standard_normal((g, D), dtype=np.float32)
-            k[b, hk] = _to_tensor(kk, dtype)
-            q[b, hk * g:(hk + 1) * g] = _to_tensor(qq, dtype)
-            if not latent:
-                v[b, hk] = _to_tensor(rng.standard_normal((Lk, Dv), dtype=np.float32), dtype)
+
+    def unit(bh):
+        b, hk = bh
+        rng = _unit_rng(seed, b, hk)
+        z = rng.integers(0, n_c, size=nK)
+        kz = np.repeat(z, TILE)[:Lk]
+        kk = r * C[kz] + sigma * rng.standard_normal((Lk, D), dtype=np.float32)
+        m = int(rng.integers(1, max_hot + 1))
+        hot = rng.choice(n_c, size=m, replace=False)
+        u = C[hot].sum(axis=0)
+        u /= np.linalg.norm(u)
+        qq = r * u[None, :] + sigma * rng.standard_normal((g, D), dtype=np.float32)
+        k[b, hk] = _to_tensor(kk, dtype)
+        q[b, hk * g:(hk + 1) * g] = _to_tensor(qq, dtype)
+        if not latent:
+            v[b, hk] = _to_tensor(rng.standard_normal((Lk, Dv), dtype=np.float32), dtype)
+
+    _for_units([(b, hk) for b in range(B) for hk in range(Hkv)], unit)
     return {"q": q, "k": k, "v": v}
 
 
@@ -146,15 +178,14 @@ def video_dit_field(seed: int, B: int, H: int, grid: tuple = (13, 42, 60), n_fie
     channels ``alpha*[cos(pi*p_a/N_a), sin(pi*p_a/N_a)]`` for each grid axis
     ``a`` are appended identically to q and k; their dot product is
     ``alpha^2 * sum_a cos(pi*(p_a - p'_a)/N_a)``, largest for nearby tokens
-    and bounded, so bf16 holds it.  V ~ N(0, 1).  Draw order per (b, head):
-    field grids, query noise, key noise, V.
+    and bounded, so bf16 holds it.  V ~ N(0, 1).  Draw order, from the
+    stream of each (b, head): field grids, query noise, key noise, V.
 
     ``heads`` generates only the first ``heads`` heads (a bounded sample of
     the full tensor, bit-identical to its leading heads).
     """
     from scipy.ndimage import gaussian_filter
 
-    rng = np.random.default_rng(seed)
     T, Hh, W = grid
     L = T * Hh * W
     D = n_field + 6
@@ -169,16 +200,19 @@ def video_dit_field(seed: int, B: int, H: int, grid: tuple = (13, 42, 60), n_fie
     q = torch.empty((B, nh, L, D), dtype=tdt)
     k = torch.empty((B, nh, L, D), dtype=tdt)
     v = torch.empty((B, nh, L, D), dtype=tdt)
-    for b in range(B):
-        for h in range(nh):
-            f = rng.standard_normal((n_field, T, Hh, W), dtype=np.float32)
-            f = gaussian_filter(f, sigma=(0, blur, blur, blur), mode="reflect")
-            f = f.reshape(n_field, L)
-            f = (f - f.mean(axis=1, keepdims=True)) / f.std(axis=1, keepdims=True)
-            F = np.ascontiguousarray(f.T)
-            qf = F + noise * rng.standard_normal((L, n_field), dtype=np.float32)
-            kf = F + noise * rng.standard_normal((L, n_field), dtype=np.float32)
-            q[b, h] = _to_tensor(np.concatenate([qf, loc], axis=1), dtype)
-            k[b, h] = _to_tensor(np.concatenate([kf, loc], axis=1), dtype)
-            v[b, h] = _to_tensor(rng.standard_normal((L, D), dtype=np.float32), dtype)
+    def unit(bh):
+        b, h = bh
+        rng = _unit_rng(seed, b, h)
+        f = rng.standard_normal((n_field, T, Hh, W), dtype=np.float32)
+        f = gaussian_filter(f, sigma=(0, blur, blur, blur), mode="reflect")
+        f = f.reshape(n_field, L)
+        f = (f - f.mean(axis=1, keepdims=True)) / f.std(axis=1, keepdims=True)
+        F = np.ascontiguousarray(f.T)
+        qf = F + noise * rng.standard_normal((L, n_field), dtype=np.float32)
+        kf = F + noise * rng.standard_normal((L, n_field), dtype=np.float32)
+        q[b, h] = _to_tensor(np.concatenate([qf, loc], axis=1), dtype)
+        k[b, h] = _to_tensor(np.concatenate([kf, loc], axis=1), dtype)
+        v[b, h] = _to_tensor(rng.standard_normal((L, D), dtype=np.float32), dtype)
+
+    _for_units([(b, h) for b in range(B) for h in range(nh)], unit)
     return {"q": q, "k": k, "v": v}

@@ -1,0 +1,210 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+computes the operating point exactly, and rejects bad arguments before
+launching anything (no GPU is touched by these tests)."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from oracle import host as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss_attn.h")
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import block_sparse_attention_online_amd as m
+
+    if not os.path.exists(m.library_path()):
+        from block_sparse_attention_online_amd.build import build
+
+        build()
+    m.lib()
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\**\s*(ss_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["ss_attn_prefill", "ss_attn_prefill_f32", "ss_attn_prefill_ex", "ss_attn_decode",
+              "ss_attn_decode_workspace_bytes", "ss_decode_num_splits", "ss_factor",
+              "ss_threshold", "ss_gate_enabled", "ss_resolve_threshold", "ss_last_error",
+              "ss_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(ss):
+    exported = subprocess.run(["nm", "-D", "--defined-only", ss.library_path()],
+                              capture_output=True, text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in exported.splitlines() if ln.strip()}
+    for n in declared_functions():
+        assert n in syms, n
+        assert hasattr(ss.lib(), n)
+
+
+def test_version(ss):
+    assert "gfx950" in ss.ss_version()
+
+
+# --------------------------------------------------------------------------- operating point
+
+@pytest.mark.parametrize("a,b,s,L", [(2.0, 0.0, 0.7, 32768), (1.5, math.log(2), 1.0, 1000),
+                                     (0.3, 4.0, 0.9, 32760), (7.0, -1.0, 0.0, 5)])
+def test_factor_calibrated_matches_closed_form(ss, a, b, s, L):
+    f = ss.ss_factor("calibrated", a=a, b=b, target_sparsity=s, seqlen=L)
+    assert f == pytest.approx(H.factor_calibrated(a, b, s), rel=1e-15)
+    assert ss.ss_threshold(f, L) == pytest.approx(H.threshold(f, L), rel=1e-15)
+
+
+def test_factor_direct_and_threshold(ss):
+    assert ss.ss_factor("direct", threshold=1e-3, seqlen=32768) == pytest.approx(32.768, rel=1e-15)
+    assert ss.ss_threshold(32.768, 32768) == pytest.approx(1e-3, rel=1e-15)
+    assert ss.ss_factor("calibrated", a=2.0, b=0.0, target_sparsity=0.5, seqlen=10) == 2.0
+
+
+@pytest.mark.parametrize("t,D", [(1.0, 0.7), (0.7, 0.7), (0.6, 0.7), (0.2, 0.7), (None, 0.7),
+                                 (None, None), (0.95, None), (0.0, 0.0)])
+def test_gate_matches_truth_table(ss, t, D):
+    assert ss.ss_gate_enabled(t, D) == H.gate_enabled(t, D)
+
+
+def test_resolve_threshold(ss):
+    # gate off -> dense
+    assert ss.ss_resolve_threshold("direct", threshold=0.01, seqlen=100, timestep=1.0,
+                                   disabled_until=0.7) == 0.0
+    # direct: the user threshold unchanged (no factor round trip)
+    assert ss.ss_resolve_threshold("direct", threshold=0.0123, seqlen=32760, timestep=0.6,
+                                   disabled_until=0.7) == pytest.approx(0.0123, rel=1e-7)
+    # calibrated: a*exp(b*s)/L
+    got = ss.ss_resolve_threshold("calibrated", a=3.0, b=2.0, target_sparsity=0.7, seqlen=32760,
+                                  timestep=0.2, disabled_until=0.7)
+    assert got == pytest.approx(3.0 * math.exp(1.4) / 32760, rel=1e-7)
+    # no timestep published while gating is configured -> dense
+    assert ss.ss_resolve_threshold("calibrated", a=3.0, b=2.0, target_sparsity=0.7, seqlen=10,
+                                   disabled_until=0.7) == 0.0
+
+
+@pytest.mark.parametrize("kw", [dict(mode="calibrated", a=1.0, b=1.0, target_sparsity=1.5),
+                                dict(mode="calibrated", a=float("nan"), b=1.0),
+                                dict(mode="calibrated", a=-1.0, b=0.0),
+                                dict(mode="direct", threshold=-1.0),
+                                dict(mode="direct", threshold=float("inf")),
+                                dict(mode="direct", threshold=0.1, seqlen=0),
+                                dict(mode=7)])
+def test_factor_rejects_bad_domain(ss, kw):
+    kw.setdefault("seqlen", 100)
+    mode = kw.pop("mode")
+    with pytest.raises(ss.SSError) as e:
+        ss.ss_factor(mode, **kw)
+    assert e.value.code == -1
+    assert ss.ss_last_error()
+
+
+def test_threshold_rejects_bad_domain(ss):
+    for f, L in [(1.0, 0), (-1.0, 10), (float("nan"), 10)]:
+        with pytest.raises(ss.SSError):
+            ss.ss_threshold(f, L)
+
+
+# --------------------------------------------------------------------------- split policy
+
+def test_split_policy_is_deterministic_and_bounded(ss):
+    # GQA decode, Llama-3.1-8B attention shape at 32K: 128 (batch, kv head) units
+    s = ss.ss_decode_num_splits(16, 32, 8, 32768, 128, 128)
+    assert s == 8
+    # shared-latent decode: 8 units, at least 8 tiles per split
+    assert ss.ss_decode_num_splits(8, 128, 1, 16384, 576, 512) == 16
+    assert ss.ss_decode_num_splits(8, 128, 1, 131072, 576, 512) == 32
+    for L in [1, 100, 128, 129, 1000, 4096, 65536]:
+        nK = -(-L // 128)
+        s = ss.ss_decode_num_splits(1, 4, 4, L, 128, 128)
+        assert 1 <= s <= nK
+    assert ss.ss_decode_num_splits(1, 3, 2, 100, 128, 128) == 0  # Hq % Hkv
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Lk,Dv,S", [(16, 32, 8, 32768, 128, 0), (2, 8, 2, 1000, 64, 3),
+                                             (1, 4, 1, 129, 128, 99), (8, 128, 1, 16384, 512, 0)])
+def test_workspace_bytes(ss, B, Hq, Hkv, Lk, Dv, S):
+    D = 576 if Dv == 512 else Dv
+    req = S or ss.ss_decode_num_splits(B, Hq, Hkv, Lk, D, Dv)
+    count = len(oracle.split_ranges(-(-Lk // 128), req))
+    o = count * B * Hq * Dv * 4
+    o = (o + 255) // 256 * 256
+    assert ss.ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, S) == o + count * B * Hq * 4
+
+
+# --------------------------------------------------------------------------- argument checks
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def prefill_call(ss, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, Hq=4, Hkv=2, Lq=256, Lk=256, D=128, Dv=128,
+             scale=0.1, causal=1, thr=0.01, mask=None)
+    a.update(over)
+    return ss.lib().ss_attn_prefill(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"], a["Hkv"],
+                                    a["Lq"], a["Lk"], a["D"], a["Dv"], a["scale"], a["causal"],
+                                    a["thr"], a["mask"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(B=0), -1), (dict(Lq=-5), -1),
+    (dict(Hq=3), -1), (dict(scale=0.0), -1), (dict(scale=float("inf")), -1),
+    (dict(thr=-0.1), -1), (dict(thr=float("nan")), -1), (dict(thr=float("inf")), -1),
+    (dict(D=96, Dv=96), -2), (dict(D=128, Dv=64), -2), (dict(Lk=(1 << 24) + 1), -1),
+])
+def test_prefill_rejects_before_launch(ss, over, code):
+    assert prefill_call(ss, **over) == code
+    assert ss.ss_last_error()
+
+
+def test_prefill_ex_rejects_unknown_order_and_dtype(ss):
+    p = ss._PrefillParams(0x1000, 0x1000, 0x1000, 0x1000, 1, 1, 1, 128, 128, 128, 128, 0.1, 0.0,
+                          0, 0, 5, None)
+    assert ss.lib().ss_attn_prefill_ex(ctypes.byref(p), None) == -1
+    p.order, p.dtype = 0, 9
+    assert ss.lib().ss_attn_prefill_ex(ctypes.byref(p), None) == -1
+    assert ss.lib().ss_attn_prefill_ex(None, None) == -1
+
+
+def decode_call(ss, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, Lk=1000, D=128, Dv=128,
+             scale=0.1, thr=0.01, S=0, mask=None, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return ss.lib().ss_attn_decode(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"], a["Hkv"],
+                                   a["Lk"], a["D"], a["Dv"], a["scale"], a["thr"], a["S"],
+                                   a["mask"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(Lk=0), -1), (dict(Hq=7), -1),
+    (dict(S=-1), -1), (dict(thr=-1.0), -1), (dict(scale=-0.5), -1),
+    (dict(v=None, Dv=256), -1),                     # latent value wider than the key row
+    (dict(Hq=48, Hkv=2), -2),                       # group of 24 heads
+    (dict(D=96, Dv=96), -2), (dict(v=None, Dv=64), -2),
+    (dict(ws=None), -4), (dict(wsb=100), -4),
+])
+def test_decode_rejects_before_launch(ss, over, code):
+    assert decode_call(ss, **over) == code
+    assert ss.ss_last_error()
+
+
+def test_binding_refuses_cpu_tensors(ss):
+    import torch
+
+    q = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ss.ss_attn_prefill(q, q, q)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ss.ss_attn_decode(q[:, :, 0], q, q)

@@ -208,7 +208,7 @@ def test_skipped_keys_have_dense_weight_below_threshold_prefill(thr, mode, order
     tile (design page, 'The skip test'): each skipped key's weight under dense
     softmax is < threshold."""
     Lq, Lk, tq, tk = 256, 512, 64, 32
-    q, k, v = prefill_inputs(41, Hq=2, Hkv=1, Lq=Lq, Lk=Lk, r=8.0)
+    q, k, v = prefill_inputs(44, Hq=2, Hkv=1, Lq=Lq, Lk=Lk, r=8.0)
     nskip = 0
     for causal in (True, False):
         res = oracle.prefill(q, k, v, 0.35, causal, thr, tq=tq, tk=tk, mode=mode, order=order)

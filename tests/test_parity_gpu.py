@@ -1,0 +1,240 @@
+"""GPU parity: the HIP kernels against the fp64 oracle, through the C ABI.
+
+Masks are graded with the margin rule (tiles within 1e-3 relative of the
+threshold may flip; every other tile must match; >= 99.9 % agreement).
+Outputs are graded against the oracle re-run with the GPU's own mask forced:
+rel-L2 <= 1e-2 for bf16 inputs, <= 1e-5 for the fp32 debug path.  Small cases
+span several tiles with ragged tails and run the oracle on everything; the
+full-size cases run the GPU on the whole call and the oracle on sampled
+query tiles / (batch, KV head) pairs.
+"""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.grading import grade_masks, rel_l2
+from synth import WORKLOADS, clustered_decode, clustered_prefill, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-5}
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import block_sparse_attention_online_amd as m
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.lib()
+    return m
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------------- prefill helpers
+
+def gpu_prefill(ss, x, scale, causal, thr, order):
+    q, k, v = (x[n].cuda() for n in "qkv")
+    B, Hq, Lq, _ = q.shape
+    Lk = k.shape[2]
+    mask = torch.full(ss.mask_shape_prefill(B, Hq, Lq, Lk), 255, dtype=torch.uint8, device="cuda")
+    out = ss.ss_attn_prefill_ex(q, k, v, scale=scale, causal=causal, threshold=thr,
+                                skip_mask=mask, order=order)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), mask.cpu().numpy()
+
+
+def check_prefill(ss, x, scale, causal, thr, order, dtype, blocks=None, name=""):
+    out, mask = gpu_prefill(ss, x, scale, causal, thr, order)
+    ref = oracle.prefill(x["q"], x["k"], x["v"], scale, causal, thr, order=order, blocks=blocks)
+    B, Hq, Lq, _ = x["q"].shape
+    if blocks is None:
+        sel_mask, sel_rows = None, np.ones((B, Hq, Lq), bool)
+    else:
+        sel_mask = np.zeros(ref["mask"].shape, bool)
+        sel_rows = np.zeros((B, Hq, Lq), bool)
+        for b, h, i in blocks:
+            sel_mask[b, h, i] = True
+            sel_rows[b, h, i * 128:(i + 1) * 128] = True
+    assert np.isin(mask, (0, 1, 2)).all(), "unwritten mask entries"
+    gr = grade_masks(mask, ref["mask"], ref["delta"], thr, sel_mask)
+    assert gr["ok"], f"{name}: mask {gr}"
+    forced = oracle.prefill(x["q"], x["k"], x["v"], scale, causal, thr, order=order,
+                            force_mask=np.where(sel_mask if sel_mask is not None else True, mask, 0),
+                            blocks=blocks)
+    err = rel_l2(out[sel_rows], forced["out"][sel_rows])
+    own = rel_l2(out[sel_rows], ref["out"][sel_rows])
+    visited = np.isin(mask, (0, 1)) if sel_mask is None else (np.isin(mask, (0, 1)) & sel_mask)
+    skip = float((mask[visited] == 1).mean()) if visited.any() else 0.0
+    log(f"[prefill {name}] thr={thr} order={order} skip={skip:.3f} rel-L2 vs forced={err:.2e} "
+        f"vs oracle mask={own:.2e} mask agreement={gr['agreement']:.4f} near={gr['near']}")
+    assert err <= TOL[dtype], f"{name}: rel-L2 {err}"
+    assert np.isfinite(out[sel_rows]).all()
+    return out, mask
+
+
+PREFILL_CASES = [
+    # name, B, Hq, Hkv, Lq, Lk, D, causal, order, r, thr
+    ("causal_gqa_ragged", 1, 4, 2, 1000, 1000, 128, True, "ascending", 9.0, 0.05),
+    ("causal_gqa_diag", 1, 4, 2, 1000, 1000, 128, True, "diag_first", 9.0, 0.05),
+    ("lq_below_lk", 2, 2, 1, 700, 1300, 128, True, "diag_first", 9.0, 0.2),
+    ("lq_above_lk", 1, 2, 2, 900, 400, 64, True, "ascending", 9.0, 0.1),
+    ("noncausal_d64_diag", 1, 3, 1, 1000, 1000, 64, False, "diag_first", 9.0, 0.01),
+    ("noncausal_ragged", 1, 2, 1, 513, 777, 128, False, "ascending", 9.0, 0.3),
+    ("thr_above_one", 1, 2, 1, 513, 777, 128, False, "ascending", 3.0, 2.0),
+    ("thr_one", 1, 2, 2, 640, 640, 128, True, "diag_first", 3.0, 1.0),
+    ("dense", 1, 4, 1, 1000, 1000, 128, True, "ascending", 3.0, 0.0),
+    ("single_tile", 1, 1, 1, 100, 100, 64, True, "ascending", 3.0, 0.5),
+    ("one_query_row", 1, 1, 1, 1, 300, 128, True, "ascending", 9.0, 0.1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_small(ss, case, dtype):
+    name, B, Hq, Hkv, Lq, Lk, D, causal, order, r, thr = case
+    x = clustered_prefill(zlib.crc32(name.encode()) % 10000, B, Hq, Hkv, Lq, Lk, D, D, 16, r, "tile", dtype=dtype)
+    check_prefill(ss, x, 1 / math.sqrt(D), causal, thr, order, dtype, name=f"{name}/{dtype}")
+
+
+@pytest.mark.parametrize("thr", [0.0, 1e-4, 1e-3])
+def test_prefill_tiny_f32_workload(ss, thr):
+    """Tiny non-causal fp32 case (B1 H1 L1024 D64, scale 1/8, 8 centroids r=3)."""
+    w = WORKLOADS["tiny_f32"]
+    x = make_inputs(w)
+    q, k, v = (x[n].cuda() for n in "qkv")
+    mask = torch.empty(ss.mask_shape_prefill(1, 1, 1024, 1024), dtype=torch.uint8, device="cuda")
+    out = ss.ss_attn_prefill_f32(q, k, v, scale=w.scale, threshold=thr, skip_mask=mask)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(x["q"], x["k"], x["v"], w.scale, False, thr)
+    gr = grade_masks(mask.cpu().numpy(), ref["mask"], ref["delta"], thr)
+    assert gr["ok"], gr
+    err = rel_l2(out.cpu().numpy(), ref["out"])
+    dense = oracle.dense_prefill(x["q"], x["k"], x["v"], w.scale, False)
+    log(f"[tiny_f32] thr={thr} skip={ref['skip_fraction']:.3f} rel-L2={err:.2e} "
+        f"vs dense={rel_l2(out.cpu().numpy(), dense):.2e}")
+    assert err <= 1e-5
+
+
+@pytest.mark.parametrize("thr", [1e-3, 1e-2, 0.1, 1.0])
+@pytest.mark.parametrize("name", ["tiny_tile_f32", "tiny_tile_bf16"])
+def test_prefill_tiny_tile_workloads(ss, name, thr):
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    check_prefill(ss, x, w.scale, w.causal, thr, "ascending", w.dtype, name=name)
+
+
+@pytest.mark.parametrize("thr,order", [(0.0, "ascending"), (0.5, "ascending"),
+                                       (0.5, "diag_first")])
+def test_prefill_gqa_16k_full_size_sampled(ss, thr, order):
+    """Causal GQA prefill at full size (B1 Hq32 Hkv8 L16384 D128); the oracle
+    checks 9 sampled query tiles across heads and positions."""
+    w = WORKLOADS["gqa_prefill_16k"]
+    x = make_inputs(w)
+    blocks = [(0, h, i) for h in (0, 13, 31) for i in (0, 37, 127)]
+    check_prefill(ss, x, w.scale, True, thr, order, "bf16", blocks=blocks, name=w.name)
+
+
+def test_prefill_video_dit_full_size_sampled(ss):
+    """Non-causal video-DiT prefill at full size (H24 L32760 D128, ragged last tile)."""
+    w = WORKLOADS["video_dit_32760"]
+    x = make_inputs(w)
+    thr = 3.0 / w.Lk
+    blocks = [(0, h, i) for h in (0, 23) for i in (0, 100, 255)]
+    for order in ("ascending", "diag_first"):
+        check_prefill(ss, x, w.scale, False, thr, order, "bf16", blocks=blocks, name=w.name)
+
+
+# --------------------------------------------------------------------------- decode
+
+def gpu_decode(ss, x, scale, thr, S, latent_dv=None):
+    q, k = x["q"].cuda(), x["k"].cuda()
+    v = None if x["v"] is None else x["v"].cuda()
+    B, Hkv, Lk = k.shape[0], k.shape[1], k.shape[2]
+    mask = torch.full(ss.mask_shape_decode(B, Hkv, Lk), 255, dtype=torch.uint8, device="cuda")
+    out = ss.ss_attn_decode(q, k, v, dv=latent_dv, scale=scale, threshold=thr, num_splits=S,
+                            skip_mask=mask)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), mask.cpu().numpy()
+
+
+def check_decode(ss, x, scale, thr, S, pairs=None, latent_dv=None, name=""):
+    out, mask = gpu_decode(ss, x, scale, thr, S, latent_dv)
+    B, Hq, D = x["q"].shape
+    Hkv, Lk = x["k"].shape[1], x["k"].shape[2]
+    Dv = latent_dv or x["v"].shape[3]
+    S_eff = S or ss.ss_decode_num_splits(B, Hq, Hkv, Lk, D, Dv)
+    ref = oracle.decode(x["q"], x["k"], x["v"], scale, thr, S_eff, latent_dv=latent_dv, pairs=pairs)
+    g = Hq // Hkv
+    if pairs is None:
+        sel_mask, sel_rows = None, np.ones((B, Hq), bool)
+    else:
+        sel_mask = np.zeros(ref["mask"].shape, bool)
+        sel_rows = np.zeros((B, Hq), bool)
+        for b, hk in pairs:
+            sel_mask[b, hk] = True
+            sel_rows[b, hk * g:(hk + 1) * g] = True
+    assert np.isin(mask, (0, 1)).all(), "unwritten decode mask entries"
+    gr = grade_masks(mask, ref["mask"], ref["delta"], thr, sel_mask)
+    assert gr["ok"], f"{name}: mask {gr}"
+    forced = oracle.decode(x["q"], x["k"], x["v"], scale, thr, S_eff, latent_dv=latent_dv,
+                           pairs=pairs, force_mask=mask)
+    err = rel_l2(out[sel_rows], forced["out"][sel_rows])
+    own = rel_l2(out[sel_rows], ref["out"][sel_rows])
+    sm = mask if sel_mask is None else mask[sel_mask]
+    log(f"[decode {name}] thr={thr} splits={S_eff} skip={float((sm == 1).mean()):.3f} "
+        f"rel-L2 vs forced={err:.2e} vs oracle mask={own:.2e} agreement={gr['agreement']:.4f}")
+    assert err <= TOL["bf16"], f"{name}: rel-L2 {err}"
+    return out, mask
+
+
+DECODE_CASES = [
+    # name, B, Hq, Hkv, Lk, D, S, r, thr
+    ("gqa4_auto", 2, 8, 2, 5000, 128, 0, 9.0, 0.05),
+    ("mha_d64", 3, 4, 4, 777, 64, 2, 9.0, 0.3),
+    ("mqa8_thr1", 1, 8, 1, 3000, 128, 5, 9.0, 1.0),
+    ("gqa8_one_split", 2, 16, 2, 4100, 128, 1, 9.0, 0.01),
+    ("one_tile", 1, 2, 1, 128, 64, 1, 3.0, 0.5),
+    ("dense", 2, 4, 2, 2000, 128, 3, 3.0, 0.0),
+    ("thr_above_one", 1, 4, 2, 3333, 64, 4, 3.0, 2.0),
+    ("one_key", 1, 2, 2, 1, 128, 1, 3.0, 0.1),
+    ("gqa2_many_splits", 1, 4, 2, 2500, 128, 99, 9.0, 0.05),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_small(ss, case):
+    name, B, Hq, Hkv, Lk, D, S, r, thr = case
+    x = clustered_decode(zlib.crc32(name.encode()) % 10000, B, Hq, Hkv, Lk, D, D, 16, r)
+    check_decode(ss, x, 1 / math.sqrt(D), thr, S, name=name)
+
+
+@pytest.mark.parametrize("thr", [0.0, 0.9])
+def test_decode_gqa_32k_full_size(ss, thr):
+    """GQA decode at full size (B16 Hq32 Hkv8 Lk32768 D128) with the automatic
+    split count; the oracle checks 24 sampled (batch, KV head) pairs."""
+    w = WORKLOADS["gqa_decode_32k"]
+    x = make_inputs(w)
+    rng = np.random.default_rng(0)
+    pairs = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, 16, 24), rng.integers(0, 8, 24))})
+    check_decode(ss, x, w.scale, thr, 0, pairs=pairs, name=w.name)
+
+
+# --------------------------------------------------------------------------- determinism
+
+def test_repeat_runs_are_bitwise_identical(ss):
+    x = clustered_prefill(5, 1, 4, 2, 1000, 1000, 128, 128, 16, 9.0, "tile")
+    a = gpu_prefill(ss, x, 1 / math.sqrt(128), True, 0.05, "diag_first")
+    b = gpu_prefill(ss, x, 1 / math.sqrt(128), True, 0.05, "diag_first")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    d = clustered_decode(6, 2, 8, 2, 5000, 128, 128, 16, 9.0)
+    c1 = gpu_decode(ss, d, 1 / math.sqrt(128), 0.05, 0)
+    c2 = gpu_decode(ss, d, 1 / math.sqrt(128), 0.05, 0)
+    assert np.array_equal(c1[0], c2[0]) and np.array_equal(c1[1], c2[1])
