@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the skip-softmax attention hot path on one MI355X.
+
+Metric: prefill TFLOP/s + decode KV GB/s at ~70 % tile skip, and the speedup
+over the same kernels at threshold 0 (dense).
+
+One step is one split-KV decode call (decode kernel + log-sum-exp combine) on
+the GQA decode workload with the Llama-3.1-8B attention shape: batch 16, 32
+query heads over 8 KV heads, head dim 128, 32768 cached keys, bf16 K/V
+resident in HBM.  The threshold is calibrated first (bisection on the
+kernel's own skip mask) to the target skip fraction.  ``value`` is the
+decode's algorithmic bytes (K, plus V of the kept tiles, plus q and out) per
+second of step wall time.  The causal GQA prefill (B1, Hq32/Hkv8, L16384,
+D128) is timed in the same run and reported under ``prefill``.
+
+``roofline`` is for the decode kernel alone, timed with HIP events on the
+stream it is launched on; ``cpu_baseline`` times the fp64 CPU oracle on a
+bounded sample of the same decode.
+
+Usage: python bench.py [--steps K] [--warmup W] [--target-skip 0.7]
+       python bench.py --copy-probe       (a plain 1 GiB device copy, for
+                                           scaling hardware byte counters)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill TFLOP/s + decode KV GB/s at ~70% tile skip; speedup vs dense"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gqa_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_online_amd", "csrc", "decode_gqa.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------- decode
+
+def decode_bytes(mask_np, B, Hq, Hkv, Lk, D, Dv, S):
+    """Algorithmic bytes of one decode call: K always; V of kept tiles; q; out;
+    and (for the decode kernel alone) the split partials it writes."""
+    import numpy as np
+
+    nK = mask_np.shape[-1]
+    keys = np.full(nK, 128, dtype=np.int64)
+    keys[-1] = Lk - 128 * (nK - 1)
+    kept_keys = int(((mask_np == 0) * keys[None, None, :]).sum())
+    k_bytes = B * Hkv * Lk * D * 2
+    v_bytes = kept_keys * Dv * 2
+    q_bytes = B * Hq * D * 2
+    out_bytes = B * Hq * Dv * 2
+    part_bytes = S * B * Hq * (Dv + 1) * 4
+    return {"k": k_bytes, "v_kept": v_bytes, "q": q_bytes, "out": out_bytes,
+            "partials": part_bytes, "v_dense": B * Hkv * Lk * Dv * 2}
+
+
+def bench_decode(ss, torch, args):
+    from block_sparse_attention_online_amd.calibrate import bisect_threshold, skip_fraction
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS["gqa_decode_32k"]
+    t = time.time()
+    x = make_inputs(w)
+    log(f"[decode] generated {w.name} in {time.time() - t:.1f}s")
+    q, k, v = (x[n].cuda() for n in "qkv")
+    B, Hq, Hkv, Lk, D, Dv = w.B, w.Hq, w.Hkv, w.Lk, w.D, w.Dv
+    S = ss.ss_decode_num_splits(B, Hq, Hkv, Lk, D, Dv)
+    ws = torch.empty(ss.ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, 0),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device="cuda")
+    mask = torch.empty(ss.mask_shape_decode(B, Hkv, Lk), dtype=torch.uint8, device="cuda")
+
+    def partial(thr):
+        ss.ss_attn_decode_partial(q, k, v, scale=w.scale, threshold=thr, skip_mask=mask,
+                                  workspace=ws)
+
+    def combine():
+        ss.ss_attn_decode_combine(ws, out, B=B, Hq=Hq, Hkv=Hkv, Lk=Lk, D=D, Dv=Dv)
+
+    def skip_at(thr):
+        partial(thr)
+        torch.cuda.synchronize()
+        return skip_fraction(mask)
+
+    if args.threshold is not None:
+        thr, reachable = args.threshold, True
+    else:
+        thr, _, reachable = bisect_threshold(skip_at, args.target_skip)
+    log(f"[decode] threshold {thr:.6g} (reachable={reachable}) splits={S}")
+
+    def timed(th, steps, warmup):
+        for _ in range(warmup):
+            partial(th)
+            combine()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e in evs:
+            e[0].record()
+            partial(th)
+            e[1].record()
+            combine()
+            e[2].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        kern = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        comb = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        return wall, kern, comb
+
+    res = {"workload": w, "S": S, "thr": thr, "reachable": reachable, "x": x}
+    if not args.only_sparse_decode:
+        res["dense"] = timed(0.0, args.steps, args.warmup)
+        log(f"[decode] dense: step {res['dense'][0]:.4f} ms, kernel {res['dense'][1]:.4f} ms")
+    res["sparse"] = timed(thr, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    res["mask"] = mask.cpu().numpy()
+    res["skip"] = skip_fraction(mask)
+    res["bytes"] = decode_bytes(res["mask"], B, Hq, Hkv, Lk, D, Dv, S)
+    log(f"[decode] sparse: step {res['sparse'][0]:.4f} ms, kernel {res['sparse'][1]:.4f} ms, "
+        f"combine {res['sparse'][2]:.4f} ms, skip {res['skip']:.3f}")
+    return res
+
+
+# --------------------------------------------------------------------------- prefill
+
+def prefill_flops(mask_np, D, Dv):
+    """Executed MFMA flops: 2*128*128*D per visited (query tile, key tile) for
+    Q.K^T, plus 2*128*128*Dv per kept tile for P.V (full tiles as issued)."""
+    visited = int((mask_np != 2).sum())
+    kept = int((mask_np == 0).sum())
+    return 2 * 128 * 128 * D * visited + 2 * 128 * 128 * Dv * kept, visited, kept
+
+
+def bench_prefill(ss, torch, args, r, order):
+    from block_sparse_attention_online_amd.calibrate import bisect_threshold, skip_fraction
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS["gqa_prefill_16k"].replace(r=r)
+    x = make_inputs(w)
+    q, k, v = (x[n].cuda() for n in "qkv")
+    out = torch.empty_like(q)
+    mask = torch.empty(ss.mask_shape_prefill(w.B, w.Hq, w.Lq, w.Lk), dtype=torch.uint8,
+                       device="cuda")
+
+    def run(thr):
+        ss.ss_attn_prefill_ex(q, k, v, out, scale=w.scale, causal=True, threshold=thr,
+                              skip_mask=mask, order=order)
+
+    def skip_at(thr):
+        run(thr)
+        torch.cuda.synchronize()
+        return skip_fraction(mask)
+
+    thr, s, reachable = bisect_threshold(skip_at, args.target_skip, iters=20, tol=0.01)
+
+    def timed(th):
+        for _ in range(max(2, args.warmup // 2)):
+            run(th)
+        torch.cuda.synchronize()
+        steps = max(5, args.steps // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run(th)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        return ms, mask.cpu().numpy()
+
+    dense_ms, dmask = timed(0.0)
+    sparse_ms, smask = timed(thr)
+    fl_d, vis, _ = prefill_flops(dmask, w.D, w.Dv)
+    fl_s, _, kept = prefill_flops(smask, w.D, w.Dv)
+    fa = 4.0 * w.B * w.Hq * w.Lq * w.Lk * w.D * 0.5
+    res = {"generator": f"clustered tile r={r:g}, {w.n_c} centroids", "order": order,
+           "threshold": thr, "threshold_reaches_target": reachable,
+           "skip_fraction": round(float((smask == 1).sum() / vis), 4),
+           "ms": round(sparse_ms, 4), "dense_ms": round(dense_ms, 4),
+           "speedup_vs_dense": round(dense_ms / sparse_ms, 3),
+           "tflops_executed": round(fl_s / sparse_ms / 1e9, 2),
+           "dense_tflops_executed": round(fl_d / dense_ms / 1e9, 2),
+           "frac_of_bf16_peak": round(fl_s / sparse_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+           "fa_convention_tflops": round(fa / sparse_ms / 1e9, 2)}
+    log(f"[prefill r={r} {order}] {res}")
+    return res
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(dec, seconds):
+    """The fp64 oracle on the same decode (all sequences, same threshold and
+    split partition), repeated until about ``seconds`` of CPU time."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = os.cpu_count() or 1
+    w, x = dec["workload"], dec["x"]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        res = oracle.decode(x["q"], x["k"], x["v"], w.scale, dec["thr"], dec["S"])
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds or reps >= 50:
+            break
+    by = decode_bytes(res["mask"], w.B, w.Hq, w.Hkv, w.Lk, w.D, w.Dv, dec["S"])
+    tot = by["k"] + by["v_kept"] + by["q"] + by["out"]
+    return {"value": round(tot * reps / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"the whole decode call ({w.B * w.Hkv} (batch, kv head) pairs, same "
+                      f"threshold and split partition) run {reps}x in {dt:.1f} s of fp64 numpy"}
+
+
+# --------------------------------------------------------------------------- main
+
+def copy_probe(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+
+
+def traffic_entry(launch_bytes):
+    """HBM bytes per decode launch from committed hardware-counter runs, or None
+    when they are missing or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--target-skip", type=float, default=0.70)
+    ap.add_argument("--threshold", type=float, default=None,
+                    help="use this decode threshold instead of calibrating")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only-sparse-decode", action="store_true",
+                    help="time only the sparse decode (for hardware-counter runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_online_amd as ss
+
+    ss.lib()
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+    if args.only_sparse_decode:
+        args.no_prefill = args.no_cpu = True
+
+    dec = bench_decode(ss, torch, args)
+    w, by = dec["workload"], dec["bytes"]
+    wall, kern, comb = dec["sparse"]
+    step_bytes = by["k"] + by["v_kept"] + by["q"] + by["out"]
+    kern_bytes = by["k"] + by["v_kept"] + by["q"] + by["partials"]
+    achieved = kern_bytes / (kern * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_entry(kern_bytes),
+            "kernel": "decode_gqa_kernel<128,4>", "kernel_ms": round(kern, 4),
+            "algorithmic_bytes_per_launch": kern_bytes}
+    line = {
+        "metric": METRIC,
+        "value": round(step_bytes / (wall * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "kv_len": w.Lk, "head_dim": w.D, "generator":
+                   f"clustered keys r={w.r:g}, {w.n_c} centroids, query near 1-3 centroids",
+                   "threshold": dec["thr"], "threshold_reaches_target": dec["reachable"],
+                   "skip_fraction": round(dec["skip"], 4), "num_splits": dec["S"]},
+        "roofline": roof,
+    }
+    if "dense" in dec:
+        dwall, dkern, _ = dec["dense"]
+        line["speedup_vs_dense"] = round(dwall / wall, 3)
+        line["dense_ms_per_step"] = round(dwall, 4)
+        dense_bytes = by["k"] + by["v_dense"] + by["q"] + by["out"]
+        line["dense_value"] = round(dense_bytes / (dwall * 1e-3) / 1e9, 1)
+    if not args.no_prefill:
+        line["prefill"] = {"workload": "gqa_prefill_16k (B1 Hq32 Hkv8 L16384 D128 causal)",
+                           "literal": bench_prefill(ss, torch, args, 3.0, "diag_first"),
+                           "wide_gap": bench_prefill(ss, torch, args, 9.0, "diag_first")}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
