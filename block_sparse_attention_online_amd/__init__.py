@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "ss_attn_prefill", "ss_attn_prefill_f32", "ss_attn_prefill_ex", "ss_attn_decode",
-    "ss_attn_decode_partial", "ss_attn_decode_combine",
+    "ss_attn_decode_ex", "ss_attn_decode_partial", "ss_attn_decode_combine", "SPLIT_MODES",
     "ss_attn_decode_workspace_bytes", "ss_decode_num_splits", "ss_factor", "ss_threshold",
     "ss_gate_enabled", "ss_resolve_threshold", "ss_last_error", "ss_version", "library_path",
     "SSError", "TILE", "ORDERS", "mask_shape_prefill", "mask_shape_decode",
@@ -53,6 +53,18 @@ class _PrefillParams(ctypes.Structure):
                 ("order", ctypes.c_int), ("skip_mask_out", ctypes.c_void_p)]
 
 
+class _DecodeParams(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("B", ctypes.c_int), ("Hq", ctypes.c_int),
+                ("Hkv", ctypes.c_int), ("Lk", ctypes.c_int), ("D", ctypes.c_int),
+                ("Dv", ctypes.c_int), ("scale", ctypes.c_float), ("threshold", ctypes.c_float),
+                ("num_splits", ctypes.c_int), ("split_mode", ctypes.c_int),
+                ("skip_mask_out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+SPLIT_MODES = {"chained": 0, "independent": 1}
+
 _LIB = None
 
 _P, _I, _F, _D, _SZ, _I64 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double,
@@ -62,9 +74,9 @@ _SIGNATURES = {
     "ss_attn_prefill_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _F, _P, _P]),
     "ss_attn_prefill_ex": (_I, [ctypes.POINTER(_PrefillParams), _P]),
     "ss_attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _P, _SZ, _P]),
-    "ss_attn_decode_partial": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _P, _SZ,
-                                    _P]),
-    "ss_attn_decode_combine": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "ss_attn_decode_ex": (_I, [ctypes.POINTER(_DecodeParams), _P]),
+    "ss_attn_decode_partial": (_I, [ctypes.POINTER(_DecodeParams), _P]),
+    "ss_attn_decode_combine": (_I, [ctypes.POINTER(_DecodeParams), _P]),
     "ss_attn_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "ss_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "ss_factor": (_I, [_I, _D, _D, _D, _D, _I64, ctypes.POINTER(_D)]),
@@ -199,7 +211,8 @@ def ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits=0) -> int:
     return int(lib().ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits))
 
 
-def _decode_args(q, k, v, dv, skip_mask, workspace, num_splits, scale):
+def _decode_params(q, k, v, out, dv, scale, threshold, num_splits, split_mode, skip_mask,
+                   workspace):
     if q.dim() != 3 or k.dim() != 4:
         raise ValueError("q must be [B, Hq, D] and k [B, Hkv, Lk, D]")
     B, Hq, D = q.shape
@@ -215,86 +228,71 @@ def _decode_args(q, k, v, dv, skip_mask, workspace, num_splits, scale):
         if v.dim() != 4 or tuple(v.shape[:3]) != (B, Hkv, Lk):
             raise ValueError(f"v must be [B, Hkv, Lk, Dv] (got {tuple(v.shape)})")
         Dv, vptr = v.shape[3], _dev(v, "v", dt)
-    mptr = None
-    if skip_mask is not None:
-        if tuple(skip_mask.shape) != mask_shape_decode(B, Hkv, Lk):
-            raise ValueError(f"skip_mask must be {mask_shape_decode(B, Hkv, Lk)}")
-        mptr = _dev(skip_mask, "skip_mask", torch.uint8)
-    need = ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    return dict(B=B, Hq=Hq, Hkv=Hkv, Lk=Lk, D=D, Dv=Dv, vptr=vptr, mptr=mptr,
-                workspace=workspace, scale=float(scale),
-                qptr=_dev(q, "q", dt), kptr=_dev(k, "k", dt))
-
-
-def ss_attn_decode_partial(q, k, v=None, *, dv=None, scale=None, threshold=0.0, num_splits=0,
-                           skip_mask=None, workspace=None, stream=None):
-    """First stage of ss_attn_decode: run every split into ``workspace`` (returned)."""
-    a = _decode_args(q, k, v, dv, skip_mask, workspace, num_splits, scale)
-    ws = a["workspace"]
-    _check(lib().ss_attn_decode_partial(a["qptr"], a["kptr"], a["vptr"], a["B"], a["Hq"], a["Hkv"],
-                                        a["Lk"], a["D"], a["Dv"], a["scale"], float(threshold),
-                                        int(num_splits), a["mptr"], _dev(ws, "workspace"),
-                                        ws.numel() * ws.element_size(), _stream(stream, q.device)))
-    return ws
-
-
-def ss_attn_decode_combine(workspace, out, *, B, Hq, Hkv, Lk, D, Dv, num_splits=0, stream=None):
-    """Second stage of ss_attn_decode: log-sum-exp merge of the split partials into ``out``."""
-    _check(lib().ss_attn_decode_combine(_dev(out, "out", torch.bfloat16), B, Hq, Hkv, Lk, D, Dv,
-                                        int(num_splits), _dev(workspace, "workspace"),
-                                        workspace.numel() * workspace.element_size(),
-                                        _stream(stream, out.device)))
-    return out
-
-
-def ss_attn_decode(q, k, v=None, out=None, *, dv=None, scale=None, threshold=0.0, num_splits=0,
-                   skip_mask=None, workspace=None, stream=None):
-    """Split-KV skip-softmax decode: q[B,Hq,D], k[B,Hkv,Lk,D], v[B,Hkv,Lk,Dv] bf16,
-    or ``v=None`` with ``dv`` for a latent cache whose value rows are the first
-    ``dv`` columns of each key row.  Returns ``out`` [B,Hq,Dv]; fills
-    ``skip_mask`` (u8 [B,Hkv,ceil(Lk/128)]) when given.  ``workspace``: a
-    uint8 GPU tensor of at least ss_attn_decode_workspace_bytes() bytes
-    (allocated here when None)."""
-    if q.dim() != 3 or k.dim() != 4:
-        raise ValueError("q must be [B, Hq, D] and k [B, Hkv, Lk, D]")
-    B, Hq, D = q.shape
-    Bk, Hkv, Lk, Dk = k.shape
-    if (Bk, Dk) != (B, D):
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)}")
-    dt = torch.bfloat16
-    if v is None:
-        if dv is None:
-            raise ValueError("v=None needs dv (value columns of the latent row)")
-        Dv, vptr = int(dv), None
-    else:
-        if v.dim() != 4 or tuple(v.shape[:3]) != (B, Hkv, Lk):
-            raise ValueError(f"v must be [B, Hkv, Lk, Dv] (got {tuple(v.shape)})")
-        Dv, vptr = v.shape[3], _dev(v, "v", dt)
-    if out is None:
-        out = torch.empty((B, Hq, Dv), dtype=dt, device=q.device)
-    elif tuple(out.shape) != (B, Hq, Dv):
+    if out is not None and tuple(out.shape) != (B, Hq, Dv):
         raise ValueError(f"out must be {(B, Hq, Dv)}")
     mptr = None
     if skip_mask is not None:
         if tuple(skip_mask.shape) != mask_shape_decode(B, Hkv, Lk):
             raise ValueError(f"skip_mask must be {mask_shape_decode(B, Hkv, Lk)}")
         mptr = _dev(skip_mask, "skip_mask", torch.uint8)
-    need = ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits)
+    if split_mode not in SPLIT_MODES:
+        raise ValueError(f"split_mode must be one of {sorted(SPLIT_MODES)}")
     if workspace is None:
+        need = ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    wbytes = workspace.numel() * workspace.element_size()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    rc = lib().ss_attn_decode(_dev(q, "q", dt), _dev(k, "k", dt), vptr, _dev(out, "out", dt), B,
-                              Hq, Hkv, Lk, D, Dv, float(scale), float(threshold), int(num_splits),
-                              mptr, _dev(workspace, "workspace"), wbytes,
-                              _stream(stream, q.device))
-    _check(rc)
+    p = _DecodeParams(_dev(q, "q", dt), _dev(k, "k", dt), vptr,
+                      None if out is None else _dev(out, "out", dt), B, Hq, Hkv, Lk, D, Dv,
+                      float(scale), float(threshold), int(num_splits), SPLIT_MODES[split_mode],
+                      mptr, _dev(workspace, "workspace"),
+                      workspace.numel() * workspace.element_size())
+    return p, workspace, (B, Hq, Dv)
+
+
+def ss_attn_decode_partial(q, k, v=None, *, dv=None, scale=None, threshold=0.0, num_splits=0,
+                           split_mode="chained", skip_mask=None, workspace=None, stream=None):
+    """First stage of the decode: run every split into ``workspace`` (returned)."""
+    p, ws, _ = _decode_params(q, k, v, None, dv, scale, threshold, num_splits, split_mode,
+                              skip_mask, workspace)
+    _check(lib().ss_attn_decode_partial(ctypes.byref(p), _stream(stream, q.device)))
+    return ws
+
+
+def ss_attn_decode_combine(q, k, workspace, out, *, v=None, dv=None, num_splits=0,
+                           split_mode="chained", stream=None):
+    """Second stage: log-sum-exp merge of the split partials into ``out``.
+    ``q``, ``k`` (and ``v`` or ``dv``) only give the sizes; they are not read."""
+    p, _, _ = _decode_params(q, k, v, out, dv, 1.0, 0.0, num_splits, split_mode, None, workspace)
+    _check(lib().ss_attn_decode_combine(ctypes.byref(p), _stream(stream, out.device)))
     return out
+
+
+def ss_attn_decode_ex(q, k, v=None, out=None, *, dv=None, scale=None, threshold=0.0,
+                      num_splits=0, split_mode="chained", skip_mask=None, workspace=None,
+                      stream=None):
+    """Split-KV skip-softmax decode: q[B,Hq,D], k[B,Hkv,Lk,D], v[B,Hkv,Lk,Dv] bf16,
+    or ``v=None`` with ``dv`` for a latent cache whose value rows are the first
+    ``dv`` columns of each key row.  Returns ``out`` [B,Hq,Dv]; fills
+    ``skip_mask`` (u8 [B,Hkv,ceil(Lk/128)]) when given.  ``split_mode``:
+    "chained" (decisions of one streaming pass) or "independent" (each split
+    restarts the running max).  ``workspace``: a uint8 GPU tensor of at least
+    ss_attn_decode_workspace_bytes() bytes (allocated here when None)."""
+    if out is None:
+        Dv = int(dv) if v is None else v.shape[3]
+        out = torch.empty((q.shape[0], q.shape[1], Dv), dtype=torch.bfloat16, device=q.device)
+    p, _, _ = _decode_params(q, k, v, out, dv, scale, threshold, num_splits, split_mode,
+                             skip_mask, workspace)
+    _check(lib().ss_attn_decode_ex(ctypes.byref(p), _stream(stream, q.device)))
+    return out
+
+
+def ss_attn_decode(q, k, v=None, out=None, *, dv=None, scale=None, threshold=0.0, num_splits=0,
+                   skip_mask=None, workspace=None, stream=None):
+    """Split-KV skip-softmax decode with chained splits (see ss_attn_decode_ex)."""
+    return ss_attn_decode_ex(q, k, v, out, dv=dv, scale=scale, threshold=threshold,
+                             num_splits=num_splits, split_mode="chained", skip_mask=skip_mask,
+                             workspace=workspace, stream=stream)
 
 
 # --------------------------------------------------------------------------- host helpers

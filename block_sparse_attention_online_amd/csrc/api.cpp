@@ -4,6 +4,8 @@
 
 #include "ss_attn.h"
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -71,20 +73,116 @@ SplitPlan plan_splits(int nK, int num_splits) {
 
 bool is_latent_decode(int D, int Dv, const void* v) { return v == nullptr && Dv <= D; }
 
-int auto_splits(int B, int Hq, int Hkv, int Lk, int D, int Dv) {
-  const int nK = (int)ceil_div(Lk, SS_TILE_KEYS);
+// Which kernel serves a decode shape, and how many tiles one split of it may
+// hold when splits are chained (its score buffer in LDS).
+enum class DecodeKernel { kNone, kGqa, kMla };
+
+DecodeKernel decode_kernel(int D, int Dv, int group, bool latent) {
+  if (ssattn::decode_gqa_supported(D, Dv, group, latent)) return DecodeKernel::kGqa;
+  if (ssattn::decode_mla_supported(D, Dv, group, latent)) return DecodeKernel::kMla;
+  return DecodeKernel::kNone;
+}
+
+int chained_max_tiles(int D, int Dv, int group, bool latent) {
+  switch (decode_kernel(D, Dv, group, latent)) {
+    case DecodeKernel::kGqa: return ssattn::decode_gqa_max_tiles(group);
+    case DecodeKernel::kMla: return ssattn::decode_mla_max_tiles(group);
+    default: return 1 << 30;
+  }
+}
+
+// Automatic split count: enough workgroups to keep all 256 compute units
+// streaming (4 resident workgroups each, 2 rounds), with no split longer than
+// a chained split may be.  Chained decisions do not depend on the count.
+int auto_splits(int B, int Hq, int Hkv, int Lk, int D, int Dv, bool latent) {
+  const int64_t nK = ceil_div(Lk, SS_TILE_KEYS);
   const int64_t units = (int64_t)B * Hkv;
-  // Workgroups wanted to keep all 256 compute units streaming: the GQA kernel
-  // is light per tile, so aim for ~4 resident workgroups per CU; the
-  // latent-cache kernel carries 128 rows of MFMA work per tile, so one per CU.
-  const int64_t want = (D >= 256) ? 256 : 1024;
-  int64_t s = ceil_div(want, units);
-  // A split restarts the running max, so keep at least 8 tiles per split.
-  int64_t cap = nK / 8;
-  if (cap < 1) cap = 1;
-  if (s > cap) s = cap;
-  if (s < 1) s = 1;
-  return (int)s;
+  const int64_t want = 2048;
+  int64_t per = ceil_div(nK * units, want);
+  const int64_t cap = chained_max_tiles(D, Dv, Hq / Hkv, latent);
+  if (per > cap) per = cap;
+  if (per < 1) per = 1;
+  return (int)ceil_div(nK, per);
+}
+
+struct DecodePlan {
+  int subs;            // sub-splits (workgroups) per (batch, KV head)
+  int tiles_per_sub;   // tiles per sub-split
+  int chain_tiles;     // tiles per chain
+  int subs_per_chain;  // sub-splits per chain
+  size_t o_off, lse_off, slot_off, timeout_off, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Cut a chain of `tiles` tiles into sub-splits of at most `cap` tiles.
+void cut_chain(int tiles, int cap, int* per, int* count) {
+  const int n = (int)ceil_div(tiles, cap);
+  *per = (int)ceil_div(tiles, n);
+  *count = (int)ceil_div(tiles, *per);
+}
+
+// Split partition and workspace layout.  Chained: one chain over the whole
+// sequence, cut into `num_splits` sub-splits (raised where a sub-split would
+// exceed the kernel's capacity).  Independent: `num_splits` chains (user
+// splits of ceil(nK/S) tiles), each cut into sub-splits within capacity.
+DecodePlan plan_decode(int B, int Hq, int Hkv, int Lk, int D, int Dv, bool latent,
+                       int num_splits, bool chained) {
+  const int nK = (int)ceil_div(Lk, SS_TILE_KEYS);
+  const int req = num_splits == 0 ? auto_splits(B, Hq, Hkv, Lk, D, Dv, latent) : num_splits;
+  const int cap = chained_max_tiles(D, Dv, Hq / Hkv, latent);
+  DecodePlan p;
+  int subs_chained = 0;
+  {
+    const SplitPlan sp = plan_splits(nK, req);
+    int per = sp.per, cnt = sp.count;
+    if (per > cap) cut_chain(nK, cap, &per, &cnt);
+    subs_chained = cnt;
+    if (chained) {
+      p.subs = cnt;
+      p.tiles_per_sub = per;
+      p.chain_tiles = nK;
+      p.subs_per_chain = cnt;
+    }
+  }
+  int subs_indep = 0;
+  {
+    const SplitPlan sp = plan_splits(nK, req);
+    int per = 0, cnt = 0;
+    cut_chain(sp.per, cap, &per, &cnt);
+    subs_indep = sp.count * cnt;
+    if (!chained) {
+      p.subs = subs_indep;
+      p.tiles_per_sub = per;
+      p.chain_tiles = sp.per;
+      p.subs_per_chain = cnt;
+    }
+  }
+  const int subs_max = subs_chained > subs_indep ? subs_chained : subs_indep;
+  const size_t rows = (size_t)subs_max * B * Hq;
+  const size_t slots = (size_t)subs_max * B * Hkv;
+  p.o_off = 0;
+  p.lse_off = align256(rows * (size_t)Dv * sizeof(float));
+  p.slot_off = p.lse_off + align256(rows * sizeof(float));
+  p.timeout_off = p.slot_off + align256(slots * (size_t)(Hq / Hkv) * sizeof(unsigned long long));
+  p.bytes = p.timeout_off + 256;
+  return p;
+}
+
+// Launch tags: nonzero and different for consecutive decode launches of this
+// process, so values published by an earlier launch (or stale workspace
+// bytes) are not read as current.  They start from a process-specific value.
+std::atomic<unsigned> g_tag{0};
+
+unsigned next_tag() {
+  unsigned t = g_tag.fetch_add(2u) + 2u;
+  if (t == 2u) {  // first use
+    const unsigned seed = (unsigned)(std::chrono::steady_clock::now().time_since_epoch().count() *
+                                     0x9E3779B97F4A7C15ull >> 32);
+    g_tag.store(seed | 1u);
+    t = g_tag.fetch_add(2u) + 2u;
+  }
+  return t | 1u;
 }
 
 int validate_prefill(const ss_prefill_params* p) {
@@ -167,8 +265,11 @@ int ss_attn_prefill_f32(const float* q, const float* k, const float* v, float* o
 }
 
 int ss_decode_num_splits(int B, int Hq, int Hkv, int Lk, int D, int Dv) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || D <= 0 || Dv <= 0 || Hq % Hkv) return 0;
-  return auto_splits(B, Hq, Hkv, Lk, D, Dv);
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || D <= 0 || Dv <= 0 || Hq % Hkv ||
+      Lk > kMaxLen)
+    return 0;
+  const bool latent = decode_kernel(D, Dv, Hq / Hkv, false) == DecodeKernel::kNone && Dv <= D;
+  return auto_splits(B, Hq, Hkv, Lk, D, Dv, latent);
 }
 
 size_t ss_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lk, int D, int Dv,
@@ -176,75 +277,73 @@ size_t ss_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lk, int D, int
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || D <= 0 || Dv <= 0 || Hq % Hkv ||
       num_splits < 0 || Lk > kMaxLen)
     return 0;
-  const int nK = (int)ceil_div(Lk, SS_TILE_KEYS);
-  const int req = num_splits == 0 ? auto_splits(B, Hq, Hkv, Lk, D, Dv) : num_splits;
-  const SplitPlan sp = plan_splits(nK, req);
-  const size_t rows = (size_t)sp.count * B * Hq;
-  // split outputs, then split lse; both fp32, the lse block 256-byte aligned
-  size_t o_bytes = rows * (size_t)Dv * sizeof(float);
-  o_bytes = (o_bytes + 255) & ~(size_t)255;
-  return o_bytes + rows * sizeof(float);
+  const bool latent = decode_kernel(D, Dv, Hq / Hkv, false) == DecodeKernel::kNone && Dv <= D;
+  return plan_decode(B, Hq, Hkv, Lk, D, Dv, latent, num_splits, true).bytes;
 }
 
 }  // extern "C"
 
 namespace {
 
-// Validate a decode call and fill the launch arguments (out may be null for
-// the partial stage).  Returns SS_OK or an error code.
-int prepare_decode(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int Lk,
-                   int D, int Dv, float scale, float threshold, int num_splits,
-                   const void* workspace, size_t workspace_bytes, bool check_inputs,
-                   ssattn::DecodeArgs* a, bool* use_gqa) {
-  if (check_inputs && (!q || !k)) return fail(SS_ERR_INVALID_ARG, "q and k must be non-null");
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || D <= 0 || Dv <= 0)
+// Validate a decode call and fill the launch arguments.  `stage_partial`
+// checks the inputs of the split kernel; the combine stage needs only sizes,
+// the workspace and out.
+int prepare_decode(const ss_decode_params* p, bool stage_partial, ssattn::DecodeArgs* a,
+                   DecodeKernel* kernel) {
+  if (!p) return fail(SS_ERR_INVALID_ARG, "params is null");
+  if (stage_partial && (!p->q || !p->k)) return fail(SS_ERR_INVALID_ARG, "q and k must be non-null");
+  if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Lk <= 0 || p->D <= 0 || p->Dv <= 0)
     return fail(SS_ERR_INVALID_ARG, "sizes must be positive");
-  if (Lk > kMaxLen) return fail(SS_ERR_INVALID_ARG, "Lk above %d is not supported", kMaxLen);
-  if (Hq % Hkv)
-    return fail(SS_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-  if (num_splits < 0) return fail(SS_ERR_INVALID_ARG, "num_splits must be >= 0");
-  if (check_inputs) {
-    if (!v && Dv > D) return fail(SS_ERR_INVALID_ARG, "v == NULL needs Dv <= D");
-    if (int rc = check_scale(scale)) return rc;
-    if (int rc = check_threshold(threshold)) return rc;
-    const int group = Hq / Hkv;
-    const bool latent = is_latent_decode(D, Dv, v);
-    const bool gqa = ssattn::decode_gqa_supported(D, Dv, group, latent);
-    const bool mla = !gqa && ssattn::decode_mla_supported(D, Dv, group, latent);
-    if (!gqa && !mla)
-      return fail(SS_ERR_UNSUPPORTED, "no decode kernel for D=%d Dv=%d group=%d %s", D, Dv,
-                  group, latent ? "(latent V)" : "(separate V)");
-    *use_gqa = gqa;
+  if (p->Lk > kMaxLen) return fail(SS_ERR_INVALID_ARG, "Lk above %d is not supported", kMaxLen);
+  if (p->Hq % p->Hkv)
+    return fail(SS_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->num_splits < 0) return fail(SS_ERR_INVALID_ARG, "num_splits must be >= 0");
+  if (p->split_mode != SS_SPLIT_CHAINED && p->split_mode != SS_SPLIT_INDEPENDENT)
+    return fail(SS_ERR_INVALID_ARG, "unknown split_mode %d", p->split_mode);
+  const bool latent = is_latent_decode(p->D, p->Dv, p->v);
+  if (stage_partial) {
+    if (!p->v && p->Dv > p->D) return fail(SS_ERR_INVALID_ARG, "v == NULL needs Dv <= D");
+    if (int rc = check_scale(p->scale)) return rc;
+    if (int rc = check_threshold(p->threshold)) return rc;
   }
-  const size_t need = ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits);
-  if (!workspace || workspace_bytes < need)
-    return fail(SS_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need,
-                workspace_bytes, workspace ? "" : ", null");
-  const int nK = (int)ceil_div(Lk, SS_TILE_KEYS);
-  const int req = num_splits == 0 ? auto_splits(B, Hq, Hkv, Lk, D, Dv) : num_splits;
-  const SplitPlan sp = plan_splits(nK, req);
-  a->q = q;
-  a->k = k;
-  a->v = v;
-  a->out = nullptr;
-  a->mask = nullptr;
-  const size_t rows = (size_t)sp.count * B * Hq;
-  size_t o_bytes = rows * (size_t)Dv * sizeof(float);
-  o_bytes = (o_bytes + 255) & ~(size_t)255;
-  char* ws = static_cast<char*>(const_cast<void*>(workspace));
-  a->part_o = reinterpret_cast<float*>(ws);
-  a->part_lse = reinterpret_cast<float*>(ws + o_bytes);
-  a->B = B;
-  a->Hq = Hq;
-  a->Hkv = Hkv;
-  a->Lk = Lk;
-  a->D = D;
-  a->Dv = Dv;
-  a->num_splits = sp.count;
-  a->tiles_per_split = sp.per;
-  a->scale = scale;
-  a->log2_thr = log2_threshold(threshold);
-  a->thr_above_1 = threshold > 1.f;
+  const int group = p->Hq / p->Hkv;
+  // the combine stage sees no v pointer: any kernel that serves the shape will do
+  DecodeKernel k = decode_kernel(p->D, p->Dv, group, stage_partial ? latent : false);
+  if (k == DecodeKernel::kNone && !stage_partial) k = decode_kernel(p->D, p->Dv, group, true);
+  if (k == DecodeKernel::kNone)
+    return fail(SS_ERR_UNSUPPORTED, "no decode kernel for D=%d Dv=%d group=%d %s", p->D, p->Dv,
+                group, latent ? "(latent V)" : "(separate V)");
+  *kernel = k;
+  const bool chained = p->split_mode == SS_SPLIT_CHAINED;
+  const DecodePlan pl = plan_decode(p->B, p->Hq, p->Hkv, p->Lk, p->D, p->Dv,
+                                    k == DecodeKernel::kMla, p->num_splits, chained);
+  if (!p->workspace || p->workspace_bytes < pl.bytes)
+    return fail(SS_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", pl.bytes,
+                p->workspace_bytes, p->workspace ? "" : ", null");
+  char* ws = static_cast<char*>(p->workspace);
+  a->q = p->q;
+  a->k = p->k;
+  a->v = p->v;
+  a->out = p->out;
+  a->mask = p->skip_mask_out;
+  a->part_o = reinterpret_cast<float*>(ws + pl.o_off);
+  a->part_lse = reinterpret_cast<float*>(ws + pl.lse_off);
+  a->lb_slot = reinterpret_cast<unsigned long long*>(ws + pl.slot_off);
+  a->lb_timeouts = reinterpret_cast<unsigned int*>(ws + pl.timeout_off);
+  a->B = p->B;
+  a->Hq = p->Hq;
+  a->Hkv = p->Hkv;
+  a->Lk = p->Lk;
+  a->D = p->D;
+  a->Dv = p->Dv;
+  a->num_splits = pl.subs;
+  a->tiles_per_split = pl.tiles_per_sub;
+  a->chain_tiles = pl.chain_tiles;
+  a->subs_per_chain = pl.subs_per_chain;
+  a->scale = p->scale;
+  a->log2_thr = log2_threshold(p->threshold);
+  a->thr_above_1 = p->threshold > 1.f;
+  a->lb_tag = 0;
   return SS_OK;
 }
 
@@ -252,47 +351,41 @@ int prepare_decode(const void* q, const void* k, const void* v, int B, int Hq, i
 
 extern "C" {
 
-int ss_attn_decode_partial(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
-                           int Lk, int D, int Dv, float scale, float threshold, int num_splits,
-                           uint8_t* skip_mask_out, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
+int ss_attn_decode_partial(const ss_decode_params* p, hipStream_t stream) {
   ssattn::DecodeArgs a;
-  bool gqa = false;
-  if (int rc = prepare_decode(q, k, v, B, Hq, Hkv, Lk, D, Dv, scale, threshold, num_splits,
-                              workspace, workspace_bytes, true, &a, &gqa))
-    return rc;
-  a.mask = skip_mask_out;
-  hipError_t e = gqa ? ssattn::launch_decode_gqa(a, stream) : ssattn::launch_decode_mla(a, stream);
+  DecodeKernel k;
+  if (int rc = prepare_decode(p, true, &a, &k)) return rc;
+  a.lb_tag = next_tag();
+  hipError_t e = k == DecodeKernel::kGqa ? ssattn::launch_decode_gqa(a, stream)
+                                         : ssattn::launch_decode_mla(a, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
 
-int ss_attn_decode_combine(void* out, int B, int Hq, int Hkv, int Lk, int D, int Dv,
-                           int num_splits, const void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
-  if (!out) return fail(SS_ERR_INVALID_ARG, "out must be non-null");
+int ss_attn_decode_combine(const ss_decode_params* p, hipStream_t stream) {
   ssattn::DecodeArgs a;
-  bool gqa = false;
-  if (int rc = prepare_decode(nullptr, nullptr, nullptr, B, Hq, Hkv, Lk, D, Dv, 1.f, 0.f,
-                              num_splits, workspace, workspace_bytes, false, &a, &gqa))
-    return rc;
-  a.out = out;
+  DecodeKernel k;
+  if (int rc = prepare_decode(p, false, &a, &k)) return rc;
+  if (!p->out) return fail(SS_ERR_INVALID_ARG, "out must be non-null");
   hipError_t e = ssattn::launch_decode_combine(a, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
+}
+
+int ss_attn_decode_ex(const ss_decode_params* p, hipStream_t stream) {
+  if (!p) return fail(SS_ERR_INVALID_ARG, "params is null");
+  if (!p->out) return fail(SS_ERR_INVALID_ARG, "out must be non-null");
+  if (int rc = ss_attn_decode_partial(p, stream)) return rc;
+  return ss_attn_decode_combine(p, stream);
 }
 
 int ss_attn_decode(const void* q, const void* k, const void* v, void* out, int B, int Hq,
                    int Hkv, int Lk, int D, int Dv, float scale, float threshold, int num_splits,
                    uint8_t* skip_mask_out, void* workspace, size_t workspace_bytes,
                    hipStream_t stream) {
-  if (!out) return fail(SS_ERR_INVALID_ARG, "out must be non-null");
-  if (int rc = ss_attn_decode_partial(q, k, v, B, Hq, Hkv, Lk, D, Dv, scale, threshold,
-                                      num_splits, skip_mask_out, workspace, workspace_bytes,
-                                      stream))
-    return rc;
-  return ss_attn_decode_combine(out, B, Hq, Hkv, Lk, D, Dv, num_splits, workspace,
-                                workspace_bytes, stream);
+  ss_decode_params p{q, k, v, out, B, Hq, Hkv, Lk, D, Dv, scale, threshold, num_splits,
+                     SS_SPLIT_CHAINED, skip_mask_out, workspace, workspace_bytes};
+  return ss_attn_decode_ex(&p, stream);
 }
 
 int ss_factor(ss_factor_mode mode, double a, double b, double target_sparsity,

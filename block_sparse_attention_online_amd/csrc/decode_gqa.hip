@@ -2,20 +2,37 @@
 // per KV head), bf16 K/V, fp32 accumulation, gfx950.
 //
 // Method: vLLM-Omni design page "Skip-Softmax", sections "The online-softmax
-// pass" and "The skip test"; BLASST summary page, section "Kerninzicht" (a
-// skipped block also skips loading its V block from HBM) and
-// "Kernel-ontwerp" (decode is memory bound; the saving is V bandwidth).
+// pass" and "The skip test"; BLASST summary page, sections "Kerninzicht" (a
+// skipped block also skips loading its V block from HBM) and "Kernel-ontwerp"
+// (decode is memory bound; V loads of blocks that pass the test are issued in
+// batches so the pipeline does not stall).
 //
-// One workgroup per (batch, KV head, split); 8 waves, each owning 16 keys of
-// every 128-key tile.  The group's G query rows are tiny, so the dot products
-// run on the vector ALUs: lane (key k, chunk c) multiplies 8 head dims of key
-// k by the same 8 dims of all G rows, and the 16 lanes of one key (8 for
-// D = 64) sum their partials with DPP row operations.  Every K load is one
-// 16-byte load per lane with 16 consecutive lanes on one 256-byte key row, so
-// a wave instruction reads whole rows.  The decision is taken for the whole
-// group (max over rows and over the 8 waves through LDS) before any V byte of
-// the tile is requested: a skipped tile's V is never loaded.  K of the next
-// tile is requested before the current tile is reduced.
+// One workgroup per (batch, KV head, sub-split of at most 64/G tiles), 4
+// waves; wave w owns keys [32w, 32w + 32) of every 128-key tile.  Sub-splits
+// form chains: in chained mode the whole sequence is one chain, in
+// independent mode each user split is one.  Three phases per workgroup:
+//
+//  1. K pass.  Scores S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (16 keys x 16
+//     query columns, G of them real).  K is loaded fully coalesced (16 lanes
+//     per 256-byte row, whole rows per wave instruction, two tiles ahead),
+//     passed 16 rows at a time through a per-wave XOR-swizzled LDS stage and
+//     read back in the MFMA operand layout.  Scores (log2 units) go to LDS; each wave's per-row
+//     maximum of every tile goes to LDS too.
+//  2. Decision.  One wave scans the chunk's tile maxima: lane t holds tile t,
+//     an exclusive prefix max over lanes gives every tile its running max, and
+//     the tile is skipped iff max over rows of (tile_max - running_max) <
+//     log2(threshold).  Kept tiles are compacted into a survivor list.
+//     Every sub-split first publishes its local maxima and reads those of the
+//     earlier sub-splits of its chain, so the decisions are exactly those of
+//     one streaming pass over the chain; the sub-splits still run in parallel
+//     and only this step waits.
+//  3. V pass.  Only survivors: lane (key, 16-byte chunk of the value row)
+//     loads whole 256-byte V rows per wave instruction, two survivor tiles in
+//     flight while one is accumulated, exponentials read back the
+//     stored scores.  The exponent reference is the sub-split's own maximum,
+//     so no rescale is needed at all.
+//
+// The split's O / l and lse go to the workspace; decode_combine merges splits.
 
 #include "device_common.h"
 #include "launch.h"
@@ -23,203 +40,329 @@
 namespace ssattn {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKeysPerWave = kTile / kWaves;  // 16
+constexpr int kKeysPerWave = kTile / kWaves;  // 32
+constexpr int kSpinCap = 1 << 21;             // look-back polls before giving up
+constexpr int kWavesPerSimd = 3;              // occupancy target: 3 workgroups per CU
+
+template <int G>
+constexpr int max_tiles() { return 64 / G; }  // score LDS: 128 keys x G x 4 B x tiles = 32 KB
+
+typedef __attribute__((ext_vector_type(4))) float f4_t;
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_gqa_kernel(DecodeArgs a) {
-  constexpr int KCH = D / 8;               // lanes per key row (16-byte chunks)
-  constexpr int KPI = 64 / KCH;            // keys per wave instruction
-  constexpr int IT = kKeysPerWave / KPI;   // instructions per wave per tile
-  static_assert(IT >= 1, "layout");
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(DecodeArgs a) {
+  constexpr int TMAX = max_tiles<G>();
+  constexpr int KS = D / 32;          // MFMA k-steps over the head dimension
+  constexpr int KL = 2 * KS;          // 16-byte K loads per lane per tile
+  constexpr int KCH = D / 8;          // V pass: lanes per value row
+  constexpr int KPI = 64 / KCH;       // V pass: keys per wave instruction
+  constexpr int IT = kKeysPerWave / KPI;
+  static_assert(G >= 1 && G <= 8 && TMAX <= 64, "group");
+  static_assert(kWaves * G * D <= TMAX * kTile * G, "reduction reuses the score area");
 
-  __shared__ float redm[2][kWaves][G];
-  __shared__ float sred[kWaves][G][D];
-  __shared__ float lred[kWaves][G];
+  __shared__ __attribute__((aligned(16))) float sc[TMAX * kTile * G];  // [tile][key][row]
+  __shared__ __attribute__((aligned(16))) unsigned char kstage[kWaves][16 * D * 2];
+  __shared__ float tpart[kWaves][TMAX][G];
+  __shared__ float s_mref[G];
+  __shared__ float s_lred[kWaves][G];
+  __shared__ int s_surv[TMAX];
+  __shared__ int s_nsurv;
 
-  const int S = a.num_splits;
-  const int split = blockIdx.x % S;
-  const int hk = (blockIdx.x / S) % a.Hkv;
-  const int b = blockIdx.x / (S * a.Hkv);
+  const int S = a.num_splits;  // sub-splits per (batch, KV head)
+  const int sub = blockIdx.x % S;
+  const int pair = blockIdx.x / S;  // b * Hkv + hk
+  const int hk = pair % a.Hkv;
+  const int b = pair / a.Hkv;
   const int nK = (a.Lk + kTile - 1) / kTile;
-  const int t0 = split * a.tiles_per_split;
-  const int t1 = min(t0 + a.tiles_per_split, nK);
+  const int chain = sub / a.subs_per_chain;
+  const int link = sub % a.subs_per_chain;
+  const int chain_t0 = chain * a.chain_tiles;
+  const int chain_t1 = min(chain_t0 + a.chain_tiles, nK);
+  const int t0 = chain_t0 + link * a.tiles_per_split;
+  const int T = max(0, min(t0 + a.tiles_per_split, chain_t1) - t0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int cch = lane % KCH;  // head-dim chunk of this lane
-  const int kq = lane / KCH;   // key slot within one instruction
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
 
-  const unsigned short* qp = static_cast<const unsigned short*>(a.q) + ((size_t)b * a.Hq + hk * G) * D;
+  if (T == 0) {  // an empty trailing link: nothing to publish, nobody waits on it
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const size_t rowid = ((size_t)sub * a.B + b) * a.Hq + hk * G + idx / D;
+      a.part_o[rowid * D + idx % D] = 0.f;
+      if (idx % D == 0) a.part_lse[rowid] = neg_inf();
+    }
+    return;
+  }
+
+  const unsigned short* qp =
+      static_cast<const unsigned short*>(a.q) + ((size_t)b * a.Hq + hk * G) * D;
   const unsigned short* kp =
-      static_cast<const unsigned short*>(a.k) + ((size_t)(b * a.Hkv + hk) * a.Lk) * D;
+      static_cast<const unsigned short*>(a.k) + ((size_t)pair * a.Lk) * D;
   const unsigned short* vp =
-      static_cast<const unsigned short*>(a.v) + ((size_t)(b * a.Hkv + hk) * a.Lk) * D;
-
+      static_cast<const unsigned short*>(a.v) + ((size_t)pair * a.Lk) * D;
   const float c = a.scale * kLog2e;
-  float qv[G][8];
+
+  // ---------------------------------------------------------------- 1. K pass
+  {
+    // Q^T as the MFMA B operand: lane holds row l16 (zero past G), dims 32 ks + 8 grp
+    bf16x8_t qb[KS];
 #pragma unroll
-  for (int r = 0; r < G; ++r) {
-    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(qp + (size_t)r * D + cch * 8);
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t u = {0u, 0u, 0u, 0u};
+      if (l16 < G) u = *reinterpret_cast<const u32x4_t*>(qp + (size_t)l16 * D + ks * 32 + grp * 8);
+      qb[ks] = as_bf16x8(u);
+    }
+    // coalesced K loads: load i covers rows [i*RPI, (i+1)*RPI) of the wave's 32
+    constexpr int RPI = 64 / KCH;  // key rows per wave instruction
+    const int lrow = lane / KCH, lch = lane % KCH;
+    // Loads are unconditional (no branch around them, so the compiler's wait
+    // counts stay exact and the prefetch stays in flight): keys past Lk read
+    // the last key row, and their scores are masked to -inf below.
+    auto load_k = [&](int tl, u32x4_t (&dst)[KL]) {
+      const int j0 = (t0 + tl) * kTile + w * kKeysPerWave;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[r][2 * e] = bf16_lo(u[e]) * c;
-      qv[r][2 * e + 1] = bf16_hi(u[e]) * c;
+      for (int i = 0; i < KL; ++i) {
+        const int key = min(j0 + i * RPI + lrow, a.Lk - 1);
+        dst[i] = *reinterpret_cast<const u32x4_t*>(kp + (size_t)key * D + lch * 8);
+      }
+    };
+    unsigned char* stage = kstage[w];
+    auto score_tile = [&](int tl, const u32x4_t (&src)[KL]) {
+      // the wave's 32 rows go through the stage 16 at a time (one MFMA block);
+      // 16-byte chunk c of stage row r sits at chunk c ^ (r & 7)
+      f32x4_t acc[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int i = blk * (KL / 2); i < (blk + 1) * (KL / 2); ++i) {
+          const int r = i * RPI + lrow - blk * 16;
+          *reinterpret_cast<u32x4_t*>(stage + r * (D * 2) + ((lch ^ (r & 7)) << 4)) = src[i];
+        }
+        __builtin_amdgcn_wave_barrier();
+        acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = ks * 4 + grp;
+          const u32x4_t kv =
+              *reinterpret_cast<const u32x4_t*>(stage + l16 * (D * 2) + ((ch ^ (l16 & 7)) << 4));
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qb[ks], acc[blk], 0,
+                                                            0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      const int jw = (t0 + tl) * kTile + w * kKeysPerWave;  // first key of this wave
+      float pm = neg_inf();
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kin = blk * 16 + grp * 4 + i;  // key within the wave's 32
+          float s = acc[blk][i] * c;
+          if (jw + kin >= a.Lk) s = neg_inf();
+          if (l16 < G) sc[(tl * kTile + w * kKeysPerWave + kin) * G + l16] = s;
+          pm = fmaxf(pm, s);
+        }
+      pm = fmaxf(pm, shfl_xor_f(pm, 16));
+      pm = fmaxf(pm, shfl_xor_f(pm, 32));
+      if (lane < G) tpart[w][tl][lane] = pm;
+    };
+    // three tiles of K in flight per wave; prefetches past the last tile
+    // re-read the last tile (cache hits) and are not used
+    u32x4_t kA[KL], kB[KL], kC[KL];
+    load_k(0, kA);
+    load_k(min(1, T - 1), kB);
+    for (int tl = 0; tl < T; tl += 3) {
+      load_k(min(tl + 2, T - 1), kC);
+      score_tile(tl, kA);
+      load_k(min(tl + 3, T - 1), kA);
+      if (tl + 1 < T) score_tile(tl + 1, kB);
+      load_k(min(tl + 4, T - 1), kB);
+      if (tl + 2 < T) score_tile(tl + 2, kC);
     }
   }
+  __syncthreads();
 
-  float m2[G], lpart[G], opart[G][8];
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    m2[r] = neg_inf();
-    lpart[r] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) opart[r][e] = 0.f;
-  }
-
-  auto key_of = [&](int j, int it) { return j * kTile + w * kKeysPerWave + it * KPI + kq; };
-  u32x4_t kcur[IT];
-  auto load_k = [&](u32x4_t (&dst)[IT], int j) {
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int key = key_of(j, it);
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (key < a.Lk) val = *reinterpret_cast<const u32x4_t*>(kp + (size_t)key * D + cch * 8);
-      dst[it] = val;
-    }
-  };
-  load_k(kcur, t0);
-
-  for (int j = t0; j < t1; ++j) {
-    const int par = (j - t0) & 1;
-    u32x4_t knext[IT];
-    if (j + 1 < t1) load_k(knext, j + 1);
-
-    // scores in log2 units, every lane of a key row holds its key's score
-    float s2[IT][G];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      float kf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = bf16_lo(kcur[it][e]);
-        kf[2 * e + 1] = bf16_hi(kcur[it][e]);
-      }
-      const bool valid = key_of(j, it) < a.Lk;
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qv[r][e], kf[e], d);
-        d = group_sum<KCH>(d);
-        s2[it][r] = valid ? d : neg_inf();
-      }
-    }
-
-    // tile max per row: over this lane's keys, the wave's key slots, the waves
+  // ---------------------------------------------------------------- 2. decision
+  if (w == 0) {
+    const bool valid = lane < T;
+    float tm[G], cmax[G];
 #pragma unroll
     for (int r = 0; r < G; ++r) {
-      float tm = s2[0][r];
+      float x = neg_inf();
+      if (valid) {
 #pragma unroll
-      for (int it = 1; it < IT; ++it) tm = fmaxf(tm, s2[it][r]);
-      tm = lanes_max_from<KCH>(tm);
-      if (lane == 0) redm[par][w][r] = tm;
+        for (int ww = 0; ww < kWaves; ++ww) x = fmaxf(x, tpart[ww][lane][r]);
+      }
+      tm[r] = x;
+      cmax[r] = lanes_max_from<1>(x);
     }
-    __syncthreads();
-    float tmax2[G];
-    float dblk = neg_inf();
+    // Publish this link's per-row maxima and fold in those of the earlier
+    // links of the chain.  Every published value is one 64-bit relaxed
+    // device-scope atomic holding (launch tag, float bits): a reader takes a
+    // value only once its tag is this launch's, so no ordering between
+    // locations (and no cache write-back fence) is needed.
+    const unsigned tag = a.lb_tag;
+    const size_t slot = (size_t)pair * S + sub;
+    if (a.subs_per_chain > 1) {
+#pragma unroll
+      for (int r = 0; r < G; ++r)
+        if (lane == r)
+          __hip_atomic_store(&a.lb_slot[slot * G + r],
+                             ((unsigned long long)tag << 32) | __float_as_uint(cmax[r]),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float prev[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) prev[r] = neg_inf();
+    for (int base = 0; base < link; base += 64) {
+      const int lk = base + lane;
+      if (lk < link) {
+        const size_t ps = (size_t)pair * S + (sub - link) + lk;
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+          int spins = 0;
+          unsigned long long v;
+          while (((v = __hip_atomic_load(&a.lb_slot[ps * G + r], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)) >> 32) != tag &&
+                 spins < kSpinCap) {
+            __builtin_amdgcn_s_sleep(1);
+            ++spins;
+          }
+          if (spins < kSpinCap)
+            prev[r] = fmaxf(prev[r], __uint_as_float((unsigned)v));
+          else
+            atomicAdd(a.lb_timeouts, 1u);
+        }
+      }
+    }
+    // running max before each tile: earlier links, then an exclusive prefix
+    // max over this link's tiles (lane t = tile t)
+    float dmax = neg_inf();
 #pragma unroll
     for (int r = 0; r < G; ++r) {
-      float tm = redm[par][0][r];
+      const float mstart = lanes_max_from<1>(prev[r]);
+      float incl = tm[r];
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) tm = fmaxf(tm, redm[par][ww][r]);
-      tmax2[r] = tm;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float up = __shfl_up(incl, off, 64);
+        if (lane >= off) incl = fmaxf(incl, up);
+      }
+      float excl = __shfl_up(incl, 1, 64);
+      if (lane == 0) excl = neg_inf();
+      const float M = fmaxf(mstart, excl);
       float dr = neg_inf();
-      if (tm != neg_inf()) dr = (m2[r] == neg_inf()) ? pos_inf() : tm - m2[r];
-      dblk = fmaxf(dblk, dr);
+      if (tm[r] != neg_inf()) dr = (M == neg_inf()) ? pos_inf() : tm[r] - M;
+      dmax = fmaxf(dmax, dr);
     }
-    const bool skip = dblk < a.log2_thr;
-    if (a.mask && tid == 0) a.mask[(size_t)(b * a.Hkv + hk) * nK + j] = skip ? 1 : 0;
+    const bool skip = dmax < a.log2_thr;
+    const bool kept = valid && !skip;
+    const unsigned long long bits = __ballot(kept);
+    const int idx = __popcll(bits & ((1ull << lane) - 1ull));
+    if (kept) s_surv[idx] = lane;
+    if (lane == 0) s_nsurv = __popcll(bits);
+    if (valid && a.mask) a.mask[(size_t)pair * nK + t0 + lane] = skip ? 1 : 0;
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+      if (lane == r) s_mref[r] = cmax[r];
+  }
+  __syncthreads();
 
-    if (!skip) {
-      u32x4_t vreg[IT];
+  // ---------------------------------------------------------------- 3. V pass
+  const int kq = lane / KCH;
+  const int cc = lane % KCH;
+  const int nsurv = s_nsurv;
+  float mref[G], o[G][8], lp[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    mref[r] = s_mref[r];
+    lp[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+  }
+  {
+    // unconditional loads as in the K pass; keys past Lk carry p = 0
+    auto load_v = [&](int si, u32x4_t (&dst)[IT]) {
+      const int j0 = (t0 + s_surv[si]) * kTile + w * kKeysPerWave;
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
-        const int key = key_of(j, it);
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (key < a.Lk) val = *reinterpret_cast<const u32x4_t*>(vp + (size_t)key * D + cch * 8);
-        vreg[it] = val;
+        const int key = min(j0 + it * KPI + kq, a.Lk - 1);
+        dst[it] = *reinterpret_cast<const u32x4_t*>(vp + (size_t)key * D + cc * 8);
       }
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        const float m2n = fmaxf(m2[r], tmax2[r]);
-        const float alpha = fast_exp2(m2[r] - m2n);  // 0 when m2 = -inf (m2n finite here)
-        lpart[r] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) opart[r][e] *= alpha;
-        m2[r] = m2n;
-      }
+    };
+    auto accum_v = [&](int si, const u32x4_t (&src)[IT]) {
+      const int tl = s_surv[si];
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
+        const int kin = w * kKeysPerWave + it * KPI + kq;
+        const float* srow = sc + (tl * kTile + kin) * G;
+        float p[G];
+        if constexpr (G == 4) {
+          const f4_t s4 = *reinterpret_cast<const f4_t*>(srow);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s4[r] - mref[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < G; ++r) p[r] = fast_exp2(srow[r] - mref[r]);
+        }
         float vf[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          vf[2 * e] = bf16_lo(vreg[it][e]);
-          vf[2 * e + 1] = bf16_hi(vreg[it][e]);
+          vf[2 * e] = bf16_lo(src[it][e]);
+          vf[2 * e + 1] = bf16_hi(src[it][e]);
         }
 #pragma unroll
         for (int r = 0; r < G; ++r) {
-          const float p = fast_exp2(s2[it][r] - m2[r]);
-          lpart[r] += p;
+          lp[r] += p[r];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) opart[r][e] = fmaf(p, vf[e], opart[r][e]);
+          for (int e = 0; e < 8; ++e) o[r][e] = fmaf(p[r], vf[e], o[r][e]);
         }
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        const float m2n = fmaxf(m2[r], tmax2[r]);
-        if (a.thr_above_1 && m2n > m2[r]) {
-          const float alpha = fast_exp2(m2[r] - m2n);
-          lpart[r] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) opart[r][e] *= alpha;
-        }
-        m2[r] = m2n;
+    };
+    if (nsurv > 0) {  // three survivor tiles of V in flight per wave
+      u32x4_t vA[IT], vB[IT], vC[IT];
+      load_v(0, vA);
+      load_v(min(1, nsurv - 1), vB);
+      for (int si = 0; si < nsurv; si += 3) {
+        load_v(min(si + 2, nsurv - 1), vC);
+        accum_v(si, vA);
+        load_v(min(si + 3, nsurv - 1), vA);
+        if (si + 1 < nsurv) accum_v(si + 1, vB);
+        load_v(min(si + 4, nsurv - 1), vB);
+        if (si + 2 < nsurv) accum_v(si + 2, vC);
       }
-    }
-    if (j + 1 < t1) {
-#pragma unroll
-      for (int it = 0; it < IT; ++it) kcur[it] = knext[it];
     }
   }
+  __syncthreads();  // the reduction below overwrites the score area
 
-  // ---- merge lanes of different key slots, then the waves, and write the split
+  // ---------------------------------------------------------------- merge and write
+  float* red = sc;  // [wave][row][D]
 #pragma unroll
   for (int r = 0; r < G; ++r) {
-    float lr = lanes_sum_from<KCH>(lpart[r]);
+    const float lr = lanes_sum_from<KCH>(lp[r]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) opart[r][e] = lanes_sum_from<KCH>(opart[r][e]);
-    if (lane < KCH) {
+    for (int e = 0; e < 8; ++e) o[r][e] = lanes_sum_from<KCH>(o[r][e]);
+    if (kq == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sred[w][r][cch * 8 + e] = opart[r][e];
+      for (int e = 0; e < 8; ++e) red[(w * G + r) * D + cc * 8 + e] = o[r][e];
     }
-    if (lane == 0) lred[w][r] = lr;
+    if (lane == 0) s_lred[w][r] = lr;
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int r = idx / D, dv = idx % D;
-    float o = 0.f, l = 0.f;
+    float ov = 0.f, l = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      o += sred[ww][r][dv];
-      l += lred[ww][r];
+      ov += red[(ww * G + r) * D + dv];
+      l += s_lred[ww][r];
     }
-    const size_t rowid = ((size_t)split * a.B + b) * a.Hq + hk * G + r;
-    a.part_o[rowid * D + dv] = o / l;
-    if (dv == 0) a.part_lse[rowid] = (m2[r] + __log2f(l)) * kLn2;
+    const size_t rowid = ((size_t)sub * a.B + b) * a.Hq + hk * G + r;
+    a.part_o[rowid * D + dv] = l > 0.f ? ov / l : 0.f;
+    if (dv == 0) a.part_lse[rowid] = l > 0.f ? (s_mref[r] + __log2f(l)) * kLn2 : neg_inf();
   }
 }
 
@@ -242,6 +385,8 @@ bool decode_gqa_supported(int D, int Dv, int group, bool latent) {
   return !latent && D == Dv && (D == 64 || D == 128) &&
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
+
+int decode_gqa_max_tiles(int group) { return 64 / group; }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;

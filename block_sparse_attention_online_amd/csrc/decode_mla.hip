@@ -10,6 +10,8 @@ namespace ssattn {
 
 bool decode_mla_supported(int, int, int, bool) { return false; }
 
+int decode_mla_max_tiles(int) { return 1; }
+
 hipError_t launch_decode_mla(const DecodeArgs&, hipStream_t) { return hipErrorInvalidValue; }
 
 }  // namespace ssattn

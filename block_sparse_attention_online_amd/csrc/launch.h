@@ -34,11 +34,18 @@ struct DecodeArgs {
   float* part_o;    // [S, B, Hq, Dv] split outputs O_s / l_s
   float* part_lse;  // [S, B, Hq]     split log-sum-exp (natural log)
   int B, Hq, Hkv, Lk, D, Dv;
-  int num_splits;       // effective number of non-empty splits
-  int tiles_per_split;  // ceil(nK / requested splits)
+  int num_splits;       // sub-splits per (batch, KV head), one workgroup each
+  int tiles_per_split;  // tiles per sub-split (the last of a chain may be shorter)
+  int chain_tiles;      // tiles per chain (a user split; the whole sequence if chained)
+  int subs_per_chain;   // sub-splits per chain
   float scale;
   float log2_thr;
   int thr_above_1;
+  // Every sub-split publishes its per-row maxima and folds in those of the
+  // earlier sub-splits of its chain before deciding.
+  unsigned lb_tag;                 // nonzero, unique per launch (wraps after 2^31)
+  unsigned long long* lb_slot;     // [S][B][Hkv][G] (tag << 32) | float bits
+  unsigned int* lb_timeouts;       // count of look-back waits that gave up
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
@@ -48,8 +55,10 @@ bool prefill_f32_supported(int D, int Dv);
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s);
 bool decode_gqa_supported(int D, int Dv, int group, bool latent);
+int decode_gqa_max_tiles(int group);  // tiles a split may hold in chained mode
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
 bool decode_mla_supported(int D, int Dv, int group, bool latent);
+int decode_mla_max_tiles(int group);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace ssattn

@@ -19,7 +19,8 @@
  * Conventions shared by every entry point:
  *  - Tensors are dense, contiguous, head-major device buffers owned by the
  *    caller; the library allocates no device memory and keeps no state other
- *    than a thread-local error string.
+ *    than a thread-local error string and a counter that numbers decode
+ *    launches.
  *  - Kernels are enqueued on `stream` and the call returns without
  *    synchronising.  A NULL stream is the default stream.
  *  - A tile is skipped iff  max over the rows of its decision block of
@@ -118,6 +119,16 @@ int ss_attn_prefill_ex(const ss_prefill_params* p, hipStream_t stream);
 
 /* ------------------------------------------------------------------ decode */
 
+/* How the key tiles of one sequence are split across workgroups.
+ * CHAINED (the default): the splits run in parallel, but every split first
+ *   publishes its tile maxima and takes the running max of all earlier splits
+ *   into its decisions, so the skip decisions are exactly those of one
+ *   streaming pass over the whole sequence -- the method as the pages state
+ *   it -- whatever the split count.
+ * INDEPENDENT: every split is its own streaming pass with its own running max
+ *   (a split restarts at -inf), so decisions depend on the split count. */
+typedef enum { SS_SPLIT_CHAINED = 0, SS_SPLIT_INDEPENDENT = 1 } ss_split_mode;
+
 /*
  * Split-KV skip-softmax decode of one query token per sequence (BLASST
  * summary, "Kerninzicht" and "Kernel-ontwerp": in decode a skipped tile also
@@ -132,41 +143,56 @@ int ss_attn_prefill_ex(const ss_prefill_params* p, hipStream_t stream);
  *
  * The key tiles are cut into num_splits contiguous splits of
  * ceil(nK / num_splits) tiles each (the last may be shorter; num_splits is
- * clamped to [1, nK] and empty trailing splits are dropped).  Each split is an
- * independent streaming pass with its own running max; a second kernel merges
- * the splits with a log-sum-exp combine.  The skip decision is uniform over
- * the Hq/Hkv query heads that share a KV head.  num_splits = 0 selects
- * ss_decode_num_splits().
+ * clamped to [1, nK] and empty trailing splits are dropped).  In CHAINED mode
+ * the count is raised where a split would exceed what one workgroup can hold
+ * (decisions do not depend on it).  A second kernel merges the splits with a
+ * log-sum-exp combine.  The skip decision is uniform over the Hq/Hkv query
+ * heads that share a KV head.  num_splits = 0 selects ss_decode_num_splits().
  *
  * `workspace` is caller-owned device memory of at least
- * ss_attn_decode_workspace_bytes() bytes (split partials); its contents on
- * entry do not matter.  Supported: (D, Dv) = (64, 64) or (128, 128) with
- * Hq/Hkv in {1, 2, 4, 8}; (576, 512) with v == NULL and Hq/Hkv a multiple of
- * 16 up to 128.
+ * ss_attn_decode_workspace_bytes() bytes; its contents on entry do not
+ * matter, and two calls that overlap in time must not share one.  Supported:
+ * (D, Dv) = (64, 64) or (128, 128) with Hq/Hkv in {1, 2, 4, 8}; (576, 512)
+ * with v == NULL and Hq/Hkv a multiple of 16 up to 128.
+ *
+ * ss_attn_decode is ss_attn_decode_ex with split_mode CHAINED.
  */
 int ss_attn_decode(const void* q, const void* k, const void* v, void* out, int B, int Hq,
                    int Hkv, int Lk, int D, int Dv, float scale, float threshold, int num_splits,
                    uint8_t* skip_mask_out, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
 
-/* The two stages of ss_attn_decode, for callers that time or schedule them
- * separately (or merge partials produced elsewhere).  ss_attn_decode_partial
- * runs every split (same arguments as ss_attn_decode minus `out`) and leaves
- * the split results in `workspace`: O_s / l_s as fp32 [S][B][Hq][Dv], then,
- * at the next 256-byte boundary, lse_s = m_s + ln l_s as fp32 [S][B][Hq],
- * with S the effective split count.  ss_attn_decode_combine merges them into
- * `out` with the log-sum-exp rule; `num_splits` and the sizes must be those
- * of the partial call. */
-int ss_attn_decode_partial(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
-                           int Lk, int D, int Dv, float scale, float threshold, int num_splits,
-                           uint8_t* skip_mask_out, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream);
-int ss_attn_decode_combine(void* out, int B, int Hq, int Hkv, int Lk, int D, int Dv,
-                           int num_splits, const void* workspace, size_t workspace_bytes,
-                           hipStream_t stream);
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v; /* NULL: latent cache, value = first Dv columns of the key row */
+  void* out;
+  int B, Hq, Hkv, Lk, D, Dv;
+  float scale;
+  float threshold;
+  int num_splits; /* 0 = automatic */
+  int split_mode; /* ss_split_mode */
+  uint8_t* skip_mask_out;
+  void* workspace;
+  size_t workspace_bytes;
+} ss_decode_params;
+
+int ss_attn_decode_ex(const ss_decode_params* p, hipStream_t stream);
+
+/* The two stages of ss_attn_decode_ex, for callers that time or schedule them
+ * separately.  ss_attn_decode_partial runs every split (p->out is not used)
+ * and leaves in the workspace, at offset 0, O_s / l_s as fp32 [S][B][Hq][Dv]
+ * and, at the next 256-byte boundary, lse_s = m_s + ln l_s as fp32
+ * [S][B][Hq] (-inf for a split whose tiles were all skipped), S being the
+ * effective split count.  ss_attn_decode_combine merges them into p->out
+ * (p->q, p->k, p->v are not used); the other fields must equal those of the
+ * partial call. */
+int ss_attn_decode_partial(const ss_decode_params* p, hipStream_t stream);
+int ss_attn_decode_combine(const ss_decode_params* p, hipStream_t stream);
 
 /* Bytes of decode workspace for these sizes (num_splits as for
- * ss_attn_decode, 0 = automatic).  Returns 0 for invalid sizes. */
+ * ss_attn_decode, 0 = automatic), enough for either split mode.  Returns 0
+ * for invalid sizes. */
 size_t ss_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lk, int D, int Dv,
                                       int num_splits);
 

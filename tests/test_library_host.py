@@ -38,6 +38,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["ss_attn_prefill", "ss_attn_prefill_f32", "ss_attn_prefill_ex", "ss_attn_decode",
+              "ss_attn_decode_ex", "ss_attn_decode_partial", "ss_attn_decode_combine",
               "ss_attn_decode_workspace_bytes", "ss_decode_num_splits", "ss_factor",
               "ss_threshold", "ss_gate_enabled", "ss_resolve_threshold", "ss_last_error",
               "ss_version"]:
@@ -120,12 +121,14 @@ def test_threshold_rejects_bad_domain(ss):
 # --------------------------------------------------------------------------- split policy
 
 def test_split_policy_is_deterministic_and_bounded(ss):
-    # GQA decode, Llama-3.1-8B attention shape at 32K: 128 (batch, kv head) units
-    s = ss.ss_decode_num_splits(16, 32, 8, 32768, 128, 128)
-    assert s == 8
-    # shared-latent decode: 8 units, at least 8 tiles per split
-    assert ss.ss_decode_num_splits(8, 128, 1, 16384, 576, 512) == 16
-    assert ss.ss_decode_num_splits(8, 128, 1, 131072, 576, 512) == 32
+    # GQA decode, Llama-3.1-8B attention shape at 32K: 128 (batch, kv head)
+    # units x 256 tiles -> 16 tiles per split (the chained capacity for a group
+    # of 4), 16 splits, 2048 workgroups
+    assert ss.ss_decode_num_splits(16, 32, 8, 32768, 128, 128) == 16
+    # small problems: one tile per split
+    assert ss.ss_decode_num_splits(1, 4, 2, 1000, 128, 128) == 8
+    # group of 1: capacity 64 tiles
+    assert ss.ss_decode_num_splits(64, 64, 64, 65536, 128, 128) == 8
     for L in [1, 100, 128, 129, 1000, 4096, 65536]:
         nK = -(-L // 128)
         s = ss.ss_decode_num_splits(1, 4, 4, L, 128, 128)
@@ -133,15 +136,22 @@ def test_split_policy_is_deterministic_and_bounded(ss):
     assert ss.ss_decode_num_splits(1, 3, 2, 100, 128, 128) == 0  # Hq % Hkv
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,Lk,Dv,S", [(16, 32, 8, 32768, 128, 0), (2, 8, 2, 1000, 64, 3),
-                                             (1, 4, 1, 129, 128, 99), (8, 128, 1, 16384, 512, 0)])
-def test_workspace_bytes(ss, B, Hq, Hkv, Lk, Dv, S):
-    D = 576 if Dv == 512 else Dv
-    req = S or ss.ss_decode_num_splits(B, Hq, Hkv, Lk, D, Dv)
-    count = len(oracle.split_ranges(-(-Lk // 128), req))
-    o = count * B * Hq * Dv * 4
-    o = (o + 255) // 256 * 256
-    assert ss.ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, S) == o + count * B * Hq * 4
+def test_workspace_bytes(ss):
+    # hand layout for B2 Hq8 Hkv2 Lk1000 D=Dv=64, 3 requested splits: 8 tiles;
+    # chained -> 3 sub-splits of 3 tiles; independent -> 3 user splits of 3
+    # tiles, each within capacity (16 tiles for a group of 4) -> 3 sub-splits
+    S = 3
+    o = S * 2 * 8 * 64 * 4          # 12288: split outputs
+    lse = S * 2 * 8 * 4             # 192 -> 256: split lse
+    slots = S * 2 * 2 * 4 * 8       # 384 -> 512: published per-row maxima (64-bit)
+    want = o + 256 + 512 + 256      # + the look-back timeout counter block
+    assert ss.ss_attn_decode_workspace_bytes(2, 8, 2, 1000, 64, 64, 3) == want
+    # long independent splits are cut into chains: 1 split of 40 tiles for a
+    # group of 4 (capacity 16) -> 3 sub-splits of 14 tiles
+    n = ss.ss_attn_decode_workspace_bytes(1, 4, 1, 5000, 128, 128, 1)
+    assert n >= 3 * 4 * 128 * 4
+    for args in [(16, 32, 8, 32768, 128, 128, 0), (2, 8, 2, 1000, 64, 64, 99)]:
+        assert ss.ss_attn_decode_workspace_bytes(*args) > 0
 
 
 # --------------------------------------------------------------------------- argument checks
@@ -180,8 +190,13 @@ def test_prefill_ex_rejects_unknown_order_and_dtype(ss):
 
 def decode_call(ss, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, Lk=1000, D=128, Dv=128,
-             scale=0.1, thr=0.01, S=0, mask=None, ws=FAKE, wsb=1 << 30)
+             scale=0.1, thr=0.01, S=0, mask=None, ws=FAKE, wsb=1 << 30, mode=0)
     a.update(over)
+    if a["mode"] != 0:
+        p = ss._DecodeParams(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"], a["Hkv"], a["Lk"],
+                             a["D"], a["Dv"], a["scale"], a["thr"], a["S"], a["mode"], a["mask"],
+                             a["ws"], a["wsb"])
+        return ss.lib().ss_attn_decode_ex(ctypes.byref(p), None)
     return ss.lib().ss_attn_decode(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"], a["Hkv"],
                                    a["Lk"], a["D"], a["Dv"], a["scale"], a["thr"], a["S"],
                                    a["mask"], a["ws"], a["wsb"], None)
@@ -193,7 +208,7 @@ def decode_call(ss, **over):
     (dict(v=None, Dv=256), -1),                     # latent value wider than the key row
     (dict(Hq=48, Hkv=2), -2),                       # group of 24 heads
     (dict(D=96, Dv=96), -2), (dict(v=None, Dv=64), -2),
-    (dict(ws=None), -4), (dict(wsb=100), -4),
+    (dict(ws=None), -4), (dict(wsb=100), -4), (dict(mode=7), -1),
 ])
 def test_decode_rejects_before_launch(ss, over, code):
     assert decode_call(ss, **over) == code

@@ -154,24 +154,36 @@ def test_prefill_video_dit_full_size_sampled(ss):
 
 # --------------------------------------------------------------------------- decode
 
-def gpu_decode(ss, x, scale, thr, S, latent_dv=None):
+def gpu_decode(ss, x, scale, thr, S, latent_dv=None, mode="chained"):
+    """Run the decode through the C ABI with a zeroed workspace; returns the
+    output, the mask and the look-back timeout count left in the workspace."""
     q, k = x["q"].cuda(), x["k"].cuda()
     v = None if x["v"] is None else x["v"].cuda()
-    B, Hkv, Lk = k.shape[0], k.shape[1], k.shape[2]
+    B, Hq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    Dv = latent_dv or v.shape[3]
     mask = torch.full(ss.mask_shape_decode(B, Hkv, Lk), 255, dtype=torch.uint8, device="cuda")
-    out = ss.ss_attn_decode(q, k, v, dv=latent_dv, scale=scale, threshold=thr, num_splits=S,
-                            skip_mask=mask)
+    nbytes = ss.ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, S)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out = ss.ss_attn_decode_ex(q, k, v, dv=latent_dv, scale=scale, threshold=thr, num_splits=S,
+                               split_mode=mode, skip_mask=mask, workspace=ws)
     torch.cuda.synchronize()
-    return out.float().cpu().numpy(), mask.cpu().numpy()
+    timeouts = int(ws[nbytes - 256:nbytes - 252].view(torch.int32).item())
+    return out.float().cpu().numpy(), mask.cpu().numpy(), timeouts
 
 
-def check_decode(ss, x, scale, thr, S, pairs=None, latent_dv=None, name=""):
-    out, mask = gpu_decode(ss, x, scale, thr, S, latent_dv)
+def check_decode(ss, x, scale, thr, S, pairs=None, latent_dv=None, name="", mode="chained"):
+    out, mask, timeouts = gpu_decode(ss, x, scale, thr, S, latent_dv, mode)
+    assert timeouts == 0, f"{name}: {timeouts} look-back waits gave up"
     B, Hq, D = x["q"].shape
     Hkv, Lk = x["k"].shape[1], x["k"].shape[2]
     Dv = latent_dv or x["v"].shape[3]
-    S_eff = S or ss.ss_decode_num_splits(B, Hq, Hkv, Lk, D, Dv)
-    ref = oracle.decode(x["q"], x["k"], x["v"], scale, thr, S_eff, latent_dv=latent_dv, pairs=pairs)
+    if mode == "chained":
+        S_ref = 1  # chained splits decide as one streaming pass
+    else:
+        S_ref = S or ss.ss_decode_num_splits(B, Hq, Hkv, Lk, D, Dv)
+    ref = oracle.decode(x["q"], x["k"], x["v"], scale, thr, S_ref, latent_dv=latent_dv,
+                        pairs=pairs)
     g = Hq // Hkv
     if pairs is None:
         sel_mask, sel_rows = None, np.ones((B, Hq), bool)
@@ -184,12 +196,12 @@ def check_decode(ss, x, scale, thr, S, pairs=None, latent_dv=None, name=""):
     assert np.isin(mask, (0, 1)).all(), "unwritten decode mask entries"
     gr = grade_masks(mask, ref["mask"], ref["delta"], thr, sel_mask)
     assert gr["ok"], f"{name}: mask {gr}"
-    forced = oracle.decode(x["q"], x["k"], x["v"], scale, thr, S_eff, latent_dv=latent_dv,
+    forced = oracle.decode(x["q"], x["k"], x["v"], scale, thr, S_ref, latent_dv=latent_dv,
                            pairs=pairs, force_mask=mask)
     err = rel_l2(out[sel_rows], forced["out"][sel_rows])
     own = rel_l2(out[sel_rows], ref["out"][sel_rows])
     sm = mask if sel_mask is None else mask[sel_mask]
-    log(f"[decode {name}] thr={thr} splits={S_eff} skip={float((sm == 1).mean()):.3f} "
+    log(f"[decode {name}] mode={mode} thr={thr} splits={S} skip={float((sm == 1).mean()):.3f} "
         f"rel-L2 vs forced={err:.2e} vs oracle mask={own:.2e} agreement={gr['agreement']:.4f}")
     assert err <= TOL["bf16"], f"{name}: rel-L2 {err}"
     return out, mask
@@ -206,25 +218,27 @@ DECODE_CASES = [
     ("thr_above_one", 1, 4, 2, 3333, 64, 4, 3.0, 2.0),
     ("one_key", 1, 2, 2, 1, 128, 1, 3.0, 0.1),
     ("gqa2_many_splits", 1, 4, 2, 2500, 128, 99, 9.0, 0.05),
+    ("g1_long_chain", 1, 2, 2, 20000, 128, 0, 9.0, 0.02),
 ]
 
 
+@pytest.mark.parametrize("mode", ["chained", "independent"])
 @pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
-def test_decode_small(ss, case):
+def test_decode_small(ss, case, mode):
     name, B, Hq, Hkv, Lk, D, S, r, thr = case
     x = clustered_decode(zlib.crc32(name.encode()) % 10000, B, Hq, Hkv, Lk, D, D, 16, r)
-    check_decode(ss, x, 1 / math.sqrt(D), thr, S, name=name)
+    check_decode(ss, x, 1 / math.sqrt(D), thr, S, name=name, mode=mode)
 
 
-@pytest.mark.parametrize("thr", [0.0, 0.9])
-def test_decode_gqa_32k_full_size(ss, thr):
+@pytest.mark.parametrize("thr,mode", [(0.0, "chained"), (0.6, "chained"), (0.95, "independent")])
+def test_decode_gqa_32k_full_size(ss, thr, mode):
     """GQA decode at full size (B16 Hq32 Hkv8 Lk32768 D128) with the automatic
     split count; the oracle checks 24 sampled (batch, KV head) pairs."""
     w = WORKLOADS["gqa_decode_32k"]
     x = make_inputs(w)
     rng = np.random.default_rng(0)
     pairs = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, 16, 24), rng.integers(0, 8, 24))})
-    check_decode(ss, x, w.scale, thr, 0, pairs=pairs, name=w.name)
+    check_decode(ss, x, w.scale, thr, 0, pairs=pairs, name=w.name, mode=mode)
 
 
 # --------------------------------------------------------------------------- determinism
@@ -235,6 +249,7 @@ def test_repeat_runs_are_bitwise_identical(ss):
     b = gpu_prefill(ss, x, 1 / math.sqrt(128), True, 0.05, "diag_first")
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     d = clustered_decode(6, 2, 8, 2, 5000, 128, 128, 16, 9.0)
-    c1 = gpu_decode(ss, d, 1 / math.sqrt(128), 0.05, 0)
-    c2 = gpu_decode(ss, d, 1 / math.sqrt(128), 0.05, 0)
-    assert np.array_equal(c1[0], c2[0]) and np.array_equal(c1[1], c2[1])
+    for mode in ("chained", "independent"):
+        c1 = gpu_decode(ss, d, 1 / math.sqrt(128), 0.05, 0, mode=mode)
+        c2 = gpu_decode(ss, d, 1 / math.sqrt(128), 0.05, 0, mode=mode)
+        assert np.array_equal(c1[0], c2[0]) and np.array_equal(c1[1], c2[1])
