@@ -69,6 +69,31 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Max over all 64 lanes, returned to every lane: DPP within each row of 16
+// lanes, then the four row results through readlane (no LDS round trips).
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppRor4>(x));
+  x = fmaxf(x, dpp<kDppRor8>(x));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Workgroup order for L2 sharing.  The hardware hands workgroup p to XCD
+// p % 8; this returns the logical work index for physical index p such that
+// each XCD owns one contiguous range of logical indices, so work items that
+// are adjacent in logical order (and read the same key/value tiles at the same
+// time) run on the same XCD, behind the same L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_local_order(int p, int n) {
+  const int x = p & 7, s = p >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return x * per + min(x, rem) + s;
+}
+
 // Max over lanes whose index differs only in bits [lo_bit, 6).
 template <int LO>
 __device__ __forceinline__ float lanes_max_from(float x) {

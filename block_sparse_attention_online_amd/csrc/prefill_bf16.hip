@@ -9,24 +9,32 @@
 // "Kernel-ontwerp": the prefill kernel skips both the softmax and the matrix
 // multiply of skipped blocks.
 //
-// Design (one workgroup = one 128-row query tile of one head, 4 waves of 32
-// rows; two workgroups share a compute unit):
-//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//    K is the A operand read from LDS, Q^T the B operand held in registers for
-//    the whole pass.  The accumulator layout then gives every lane one query
-//    row and 16 keys per 32-key block, so the row max, the running state and
-//    the exponentials stay in the lane that owns the row.
-//  * The output is accumulated transposed too, O^T += V^T P^T: the lane's
-//    exponentials P are already laid out as the B operand (its row, 8 keys);
-//    V^T is the A operand, staged in LDS transposed with the 4-key groups of
-//    every 16 keys ordered so that each lane's 8 keys are one 16-byte read.
-//  * LDS tiles use an XOR swizzle of 16-byte chunks so the MFMA operand reads
-//    (8 lanes on 8 different rows, same column) hit distinct banks.
+// Design (one workgroup = one 128-row query tile of NH query heads that share
+// a KV head -- NH = 2 at D = 64 when the group size is even, else 1 -- 4 waves
+// of 32 rows, one workgroup per compute unit):
+//  * The NH heads visit the same key/value tiles in the same order, so every
+//    tile brought into LDS serves all of them; each head keeps its own
+//    128-row skip decision and its own running state.
+//  * K and V tiles move from global memory straight into LDS
+//    (global_load_lds, 16 bytes per lane, no registers), into a two-stage
+//    ring: the next tile's loads are in flight while the current tile is
+//    multiplied.  Which lane fetches which 16-byte chunk is permuted so the
+//    LDS image is XOR-swizzled for conflict-free operand reads.
+//  * Scores are computed transposed, S^T = K Q^T with
+//    v_mfma_f32_32x32x16_bf16: K is the A operand (16-byte LDS reads), Q^T the
+//    B operand held in registers for the whole pass.  The accumulator layout
+//    gives every lane one query row and 16 keys per 32-key block, so the row
+//    max, the running state and the exponentials stay in the lane that owns
+//    the row.
+//  * The output is accumulated transposed too, O^T += V^T P^T: the lane's bf16
+//    exponentials are already the B operand (its row, 8 keys); the V^T A
+//    operand comes from the row-major V tile through ds_read_b64_tr_b16
+//    transpose reads (each 16-lane group turns 4 keys x 16 value columns into
+//    4 keys per column).
 //  * The skip decision: per row delta = tile_max - m (log2 units), the max over
 //    the wave's 32 rows by shuffles, the max over the 4 waves through LDS;
 //    skip when it is below log2(threshold).  The branch is uniform over the
 //    workgroup, so a skipped tile issues no exp and no P.V MFMA at all.
-//  * K for the next tile is prefetched into registers during the current one.
 
 #include "device_common.h"
 #include "launch.h"
@@ -37,42 +45,49 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-// Byte offset of 16-byte chunk `c` of row `r` in a swizzled LDS tile whose
-// rows are `row_bytes` long.
-__device__ __forceinline__ int swz(int r, int c, int row_bytes) {
-  return r * row_bytes + ((c ^ (r & 7)) << 4);
-}
-// V^T rows are the value columns; both the transposing writes (8 rows 8
-// apart) and the operand reads (8 consecutive rows) must spread over chunks.
-__device__ __forceinline__ int vt_swz(int dv, int c) {
-  return dv * (kTile * 2) + ((c ^ ((dv ^ (dv >> 3)) & 7)) << 4);
-}
-// Slot of 4-key group `a` (0..3) inside its 16-key group in the V^T layout:
-// groups 1 and 2 trade places, so MFMA lane half g reads keys
-// {4g..4g+3, 8+4g..8+4g+3} of the group as one contiguous 16-byte chunk.
-__device__ __forceinline__ int quad_slot(int a) { return (a == 1) ? 2 : (a == 2 ? 1 : a); }
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-template <int D>
+// Physical 16-byte chunk of logical chunk c in row r of the K image
+// (A-operand reads: 8 lanes on 8 consecutive rows, same logical chunk).
+__device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r & 7); }
+// ... of the V image (transpose reads: 4 consecutive rows x 32 bytes).
+__device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r & 3) << 1); }
+
+template <int D, int NH>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int KCH = D / 8;        // 16-byte chunks per K row
-  constexpr int KS = D / 16;        // MFMA k-steps over the head dimension
-  constexpr int MB = D / 32;        // 32-wide value-column blocks
-  constexpr int KROW = D * 2;       // bytes per K row in LDS
-  constexpr int K_LOADS = (kTile * KCH) / kThreads;       // 16-byte K loads per thread
-  constexpr int V_UNITS = (kTile / 4) * KCH / kThreads;   // (4 keys x 8 cols) units per thread
-  static_assert(K_LOADS >= 1 && V_UNITS >= 1, "tile split");
+  constexpr int KCH = D / 8;                 // 16-byte chunks per row
+  constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
+  constexpr int MB = D / 32;                 // 32-wide value-column blocks
+  constexpr int ROW = D * 2;                 // bytes per row
+  constexpr int TILE_BYTES = kTile * ROW;    // one K or V tile
+  constexpr int ROWS_PER_LOAD = 64 / KCH;    // rows one wave instruction covers
+  constexpr int LOADS = kTile / ROWS_PER_LOAD / kWaves;  // per wave per tile (each of K, V)
 
-  __shared__ __attribute__((aligned(16))) unsigned char Ks[kTile * KROW];
-  __shared__ __attribute__((aligned(16))) unsigned char Vt[D * kTile * 2];
-  __shared__ float red[kWaves];
+  // Two-stage ring.  Each stage is its own LDS object, and the tile loop is
+  // unrolled by two so every access names its stage at compile time: then the
+  // compiler can tell that reads of one stage do not wait for the
+  // direct-to-LDS loads still filling the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char kst0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char kst1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst1[TILE_BYTES];
+  __shared__ float red[NH][kWaves];
 
   const int nQ = (a.Lq + kTile - 1) / kTile;
-  // heaviest (most tiles) query tiles first when causal
-  const int qi = blockIdx.x % nQ;
+  // Logical order: (batch, KV head, query tile, head set within the group), so
+  // the head sets of one group on one query tile -- identical key/value tile
+  // sequences -- and then neighbouring query tiles are adjacent and, through
+  // xcd_local_order, share an XCD's L2.  Heaviest query tiles first when causal.
+  const int grp_sz = a.Hq / a.Hkv;
+  const int sets = grp_sz / NH;
+  const int L = xcd_local_order(blockIdx.x, gridDim.x);
+  const int hs = L % sets;
+  const int qi = (L / sets) % nQ;
+  const int hk = (L / (sets * nQ)) % a.Hkv;
+  const int b = L / (sets * nQ * a.Hkv);
+  const int h0 = hk * grp_sz + hs * NH;  // first head of the set
   const int qtile = a.causal ? nQ - 1 - qi : qi;
-  const int h = (blockIdx.x / nQ) % a.Hq;
-  const int b = blockIdx.x / (nQ * a.Hq);
-  const int hk = h / (a.Hq / a.Hkv);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,213 +99,239 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   const bool row_ok = rq < a.Lq;
   const int shift = a.Lk - a.Lq;
 
-  const unsigned short* qp =
-      static_cast<const unsigned short*>(a.q) + ((size_t)(b * a.Hq + h) * a.Lq) * D;
   const unsigned short* kp =
       static_cast<const unsigned short*>(a.k) + ((size_t)(b * a.Hkv + hk) * a.Lk) * D;
   const unsigned short* vp =
       static_cast<const unsigned short*>(a.v) + ((size_t)(b * a.Hkv + hk) * a.Lk) * D;
-  unsigned short* op = static_cast<unsigned short*>(a.out) + ((size_t)(b * a.Hq + h) * a.Lq) * D;
 
   const VisitPlan plan = make_visit_plan(qtile, a.Lq, a.Lk, a.causal, a.order);
   const int nK = plan.nK;
-  uint8_t* mrow = a.mask ? a.mask + ((size_t)(b * a.Hq + h) * nQ + qtile) * nK : nullptr;
-  if (mrow && plan.causal) {
-    for (int j = plan.last + 1 + tid; j < nK; j += kThreads) mrow[j] = 2;
+  uint8_t* mrows[NH];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    mrows[hh] = a.mask ? a.mask + ((size_t)(b * a.Hq + h0 + hh) * nQ + qtile) * nK : nullptr;
+    if (mrows[hh] && plan.causal) {
+      for (int j = plan.last + 1 + tid; j < nK; j += kThreads) mrows[hh][j] = 2;
+    }
   }
 
-  // Q^T operand: lane holds row rq, head dims [16 ks + 8 g, +8) for every k-step
-  bf16x8_t qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4_t u = {0u, 0u, 0u, 0u};
-    if (row_ok) u = *reinterpret_cast<const u32x4_t*>(qp + (size_t)rq * D + ks * 16 + g * 8);
-    qf[ks] = as_bf16x8(u);
-  }
-
-  f32x16_t oacc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[mb][i] = 0.f;
-
-  const float c = a.scale * kLog2e;  // raw score -> log2 units
-  float m2 = neg_inf();             // running max of this lane's row (log2 units)
-  float lpart = 0.f;                // this lane's half of the row's denominator
-
-  // K prefetch registers: thread loads chunk (row, col) = divmod(tid + 256 i, KCH)
-  u32x4_t kreg[K_LOADS];
-  auto load_k = [&](int j) {
+  // Issue the direct-to-LDS loads of tile j into ring stage st.  Wave w covers
+  // rows [w * LOADS * ROWS_PER_LOAD, ...); lane l of load i writes LDS row
+  // (base row + l / KCH), physical chunk l % KCH, and fetches the logical
+  // chunk that the swizzle puts there.  Rows past Lk read the last key row
+  // (their scores are masked to -inf, their P is 0).
+  auto issue_tile = [&](int j, unsigned char* kdst0, unsigned char* vdst0) {
     const int j0 = j * kTile;
+    const int lr = lane / KCH, pc = lane % KCH;
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int u = tid + kThreads * i;
-      const int r = u / KCH, cc = u % KCH;
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (j0 + r < a.Lk) val = *reinterpret_cast<const u32x4_t*>(kp + (size_t)(j0 + r) * D + cc * 8);
-      kreg[i] = val;
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = (w * LOADS + i) * ROWS_PER_LOAD + lr;
+      const int key = min(j0 + r, a.Lk - 1);
+      const int kc = pc ^ (r & 7);         // inverse of k_slot (an involution)
+      const int vc = pc ^ ((r & 3) << 1);  // inverse of v_slot
+      const int off = (w * LOADS + i) * ROWS_PER_LOAD * ROW;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(kp + (size_t)key * D + kc * 8),
+          (void __attribute__((address_space(3)))*)(kdst0 + off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(vp + (size_t)key * D + vc * 8),
+          (void __attribute__((address_space(3)))*)(vdst0 + off), 16, 0, 0);
     }
   };
 
-  if (plan.count > 0) load_k(plan.tile_at(0));
-
-  for (int t = 0; t < plan.count; ++t) {
-    const int j = plan.tile_at(t);
-    const int j0 = j * kTile;
-    __syncthreads();  // previous tile's LDS reads are done
+  // Q^T operands: lane holds row rq, head dims [16 ks + 8 g, +8) for every k-step
+  bf16x8_t qf[NH][KS];
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int u = tid + kThreads * i;
-      const int r = u / KCH, cc = u % KCH;
-      *reinterpret_cast<u32x4_t*>(Ks + swz(r, cc, KROW)) = kreg[i];
+  for (int hh = 0; hh < NH; ++hh) {
+    const unsigned short* qp =
+        static_cast<const unsigned short*>(a.q) + ((size_t)(b * a.Hq + h0 + hh) * a.Lq) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t u = {0u, 0u, 0u, 0u};
+      if (row_ok) u = *reinterpret_cast<const u32x4_t*>(qp + (size_t)rq * D + ks * 16 + g * 8);
+      qf[hh][ks] = as_bf16x8(u);
     }
-    // V of this tile, 4 keys x 8 value columns per unit
-    u32x4_t vreg[V_UNITS][4];
-#pragma unroll
-    for (int i = 0; i < V_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int oc = u % KCH, quad = u / KCH;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = j0 + quad * 4 + kk;
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (key < a.Lk) val = *reinterpret_cast<const u32x4_t*>(vp + (size_t)key * D + oc * 8);
-        vreg[i][kk] = val;
-      }
-    }
-    __syncthreads();  // K tile visible
-
-    // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 rows
-    f32x16_t sacc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int kr = kb * 32 + l32;
-        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(Ks + swz(kr, ks * 2 + g, KROW));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[ks], sacc[kb], 0, 0, 0);
-      }
-    }
-
-    // ---- mask: keys past Lk, and causal keys past row + shift
-    const bool need_mask = (j0 + kTile > a.Lk) || (a.causal && j0 + kTile - 1 > row0 + shift);
-    if (need_mask) {
-      const int lim = a.causal ? min(a.Lk - 1, rq + shift) : a.Lk - 1;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          if (key > lim) sacc[kb][i] = neg_inf();
-        }
-    }
-
-    // ---- tile max of the row (raw units), both lane halves
-    float tmax = neg_inf();
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-    const float tmax2 = tmax * c;
-
-    float delta = neg_inf();
-    if (row_ok && tmax2 != neg_inf()) delta = (m2 == neg_inf()) ? pos_inf() : tmax2 - m2;
-    delta = lanes_max_from<1>(delta);
-    if (lane == 0) red[w] = delta;
-
-    // V^T tile: for each of the 8 columns of a unit, the unit's 4 keys as 8 bytes
-#pragma unroll
-    for (int i = 0; i < V_UNITS; ++i) {
-      const int u = tid + kThreads * i;
-      const int oc = u % KCH, quad = u / KCH;
-      const int grp = quad >> 2;                    // 16-key group
-      const int slot = grp * 4 + quad_slot(quad & 3);  // 4-key slot in the row
-      const int chunk = slot >> 1, within = (slot & 1) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int word = e >> 1;
-        const bool hi = e & 1;
-        unsigned int x[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) x[kk] = hi ? (vreg[i][kk][word] >> 16) : (vreg[i][kk][word] & 0xffffu);
-        u32x2_t pk = {x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
-        const int dv = oc * 8 + e;
-        *reinterpret_cast<u32x2_t*>(Vt + vt_swz(dv, chunk) + within) = pk;
-      }
-    }
-    // next K tile in flight during the decision, the exponentials and P.V
-    if (t + 1 < plan.count) load_k(plan.tile_at(t + 1));
-    __syncthreads();  // red[] and V^T visible
-
-    const float dblk = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const bool skip = dblk < a.log2_thr;
-    if (mrow && tid == 0) mrow[j] = skip ? 1 : 0;
-
-    const float m2_new = fmaxf(m2, tmax2);
-    if (!skip) {
-      const float mref = (m2_new == neg_inf()) ? 0.f : m2_new;
-      const float alpha = fast_exp2(m2 - mref);
-      float lsum = 0.f;
-      bf16x8_t pb[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          unsigned int pw[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(fmaf(sacc[kb][hh * 8 + 2 * e], c, -mref));
-            const float p1 = fast_exp2(fmaf(sacc[kb][hh * 8 + 2 * e + 1], c, -mref));
-            lsum += p0 + p1;
-            pw[e] = pack_bf16x2(p0, p1);
-          }
-          u32x4_t pu = {pw[0], pw[1], pw[2], pw[3]};
-          pb[kb][hh] = as_bf16x8(pu);
-        }
-      }
-      lpart = fmaf(alpha, lpart, lsum);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const int dv = mb * 32 + l32;
-            const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(Vt + vt_swz(dv, kb * 4 + hh * 2 + g));
-            oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), pb[kb][hh], oacc[mb], 0, 0, 0);
-          }
-    } else if (a.thr_above_1 && m2_new > m2) {
-      const float alpha = fast_exp2(m2 - m2_new);
-      lpart *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
-    }
-    m2 = m2_new;
   }
 
-  // ---- epilogue: O / l, lane holds columns 32 mb + 8 (i/4) + 4 g + i%4 of row rq
-  const float l = lpart + shfl_xor_f(lpart, 32);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (row_ok) {
+  f32x16_t oacc[NH][MB];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int col = mb * 32 + i4 * 8 + g * 4;
-        u32x2_t pk = {pack_bf16x2(oacc[mb][i4 * 4 + 0] * inv, oacc[mb][i4 * 4 + 1] * inv),
-                      pack_bf16x2(oacc[mb][i4 * 4 + 2] * inv, oacc[mb][i4 * 4 + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(op + (size_t)rq * D + col) = pk;
+      for (int i = 0; i < 16; ++i) oacc[hh][mb][i] = 0.f;
+
+  const float c = a.scale * kLog2e;  // raw score -> log2 units
+  float m2[NH], lpart[NH];          // per head: running max (log2 units), this lane's
+#pragma unroll                      // half of the row's denominator
+  for (int hh = 0; hh < NH; ++hh) {
+    m2[hh] = neg_inf();
+    lpart[hh] = 0.f;
+  }
+
+  if (plan.count > 0) issue_tile(plan.tile_at(0), kst0, vst0);
+
+  // one tile; Ks/Vs: this tile's stage, Kn/Vn: the other stage
+  auto step = [&](int t, const unsigned char* Ks, const unsigned char* Vs, unsigned char* Kn,
+                  unsigned char* Vn) {
+    const int j = plan.tile_at(t);
+    const int j0 = j * kTile;
+    // this tile's loads have landed (own wave), and every wave is past tile t-1
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // the stage of tile t-1 is free: start tile t+1
+    if (t + 1 < plan.count) issue_tile(plan.tile_at(t + 1), Kn, Vn);
+
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 rows (K operands read from
+      // LDS just before each block's MFMAs)
+      f32x16_t sacc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        u32x4_t kop[KS];
+        const int kr = kb * 32 + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kop[ks] = *reinterpret_cast<const u32x4_t*>(Ks + kr * ROW + (k_slot(kr, ks * 2 + g) << 4));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), qf[hh][ks],
+                                                            sacc[kb], 0, 0, 0);
       }
+
+      // ---- mask: keys past Lk, and causal keys past row + shift
+      const bool need_mask = (j0 + kTile > a.Lk) || (a.causal && j0 + kTile - 1 > row0 + shift);
+      if (need_mask) {
+        const int lim = a.causal ? min(a.Lk - 1, rq + shift) : a.Lk - 1;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = j0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+            if (key > lim) sacc[kb][i] = neg_inf();
+          }
+      }
+
+      // ---- tile max of the row (raw units), both lane halves
+      float tmax = neg_inf();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+      const float tmax2 = tmax * c;
+
+      float delta = neg_inf();
+      if (row_ok && tmax2 != neg_inf()) delta = (m2[hh] == neg_inf()) ? pos_inf() : tmax2 - m2[hh];
+      delta = wave_max(delta);
+      if (lane == 0) red[hh][w] = delta;
+      __syncthreads();  // red[] visible
+      const float dblk = fmaxf(fmaxf(red[hh][0], red[hh][1]), fmaxf(red[hh][2], red[hh][3]));
+      const bool skip = dblk < a.log2_thr;
+      if (mrows[hh] && tid == 0) mrows[hh][j] = skip ? 1 : 0;
+
+      const float m2n = fmaxf(m2[hh], tmax2);
+      if (!skip) {
+        const float mref = (m2n == neg_inf()) ? 0.f : m2n;
+        // rescale only when some row's running max grew (the factor is
+        // exactly 1 for every other row)
+        if (__builtin_amdgcn_ballot_w64(m2n != m2[hh]) != 0) {
+          const float alpha = fast_exp2(m2[hh] - mref);
+          lpart[hh] *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[hh][mb][i] *= alpha;
+        }
+        // ---- per 32-key block: exponentials, then O^T += V^T P^T (two 16-key
+        // steps).  V^T operands come from transpose reads; those of the next
+        // (block, step) are read while the current MFMAs run.
+        const int r16 = lane & 15;
+        const int colq = ((lane >> 4) & 1) * 16 + (r16 & 3) * 4;  // first of 4 columns
+        auto read_v = [&](int kb, int half, u32x4_t (&dst)[MB]) {
+          // keys of this lane half: {4g..4g+3} and {8+4g..8+4g+3} of the 16-key step
+          const int ra = kb * 32 + half * 16 + g * 4 + (r16 >> 2);
+          const int rb = ra + 8;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const int col = mb * 32 + colq;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t*)(Vs + ra * ROW + (v_slot(ra, col >> 3) << 4) + (col & 7) * 2));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t*)(Vs + rb * ROW + (v_slot(rb, col >> 3) << 4) + (col & 7) * 2));
+            const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+            const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+            dst[mb] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+          }
+        };
+        u32x4_t vop[2][MB];
+        read_v(0, 0, vop[0]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          bf16x8_t pb[2];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            unsigned int pw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e], c, -mref));
+              const float p1 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e + 1], c, -mref));
+              lpart[hh] += p0 + p1;
+              pw[e] = pack_bf16x2(p0, p1);
+            }
+            u32x4_t pu = {pw[0], pw[1], pw[2], pw[3]};
+            pb[half] = as_bf16x8(pu);
+          }
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int st = kb * 2 + half;
+            if (st + 1 < 8) read_v((st + 1) >> 1, (st + 1) & 1, vop[(st + 1) & 1]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              oacc[hh][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[st & 1][mb]),
+                                                                    pb[half], oacc[hh][mb], 0, 0, 0);
+          }
+        }
+      } else if (a.thr_above_1 && m2n > m2[hh]) {
+        const float alpha = fast_exp2(m2[hh] - m2n);
+        lpart[hh] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[hh][mb][i] *= alpha;
+      }
+      m2[hh] = m2n;
+      // keep the heads' live ranges apart: one set of score accumulators
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int t = 0; t < plan.count; t += 2) {
+    step(t, kst0, vst0, kst1, vst1);
+    if (t + 1 < plan.count) step(t + 1, kst1, vst1, kst0, vst0);
+  }
+
+  // ---- epilogue: O / l, lane holds columns 32 mb + 8 (i/4) + 4 g + i%4 of row rq
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    const float l = lpart[hh] + shfl_xor_f(lpart[hh], 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    unsigned short* op =
+        static_cast<unsigned short*>(a.out) + ((size_t)(b * a.Hq + h0 + hh) * a.Lq) * D;
+    if (row_ok) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int col = mb * 32 + i4 * 8 + g * 4;
+          u32x2_t pk = {pack_bf16x2(oacc[hh][mb][i4 * 4 + 0] * inv, oacc[hh][mb][i4 * 4 + 1] * inv),
+                        pack_bf16x2(oacc[hh][mb][i4 * 4 + 2] * inv, oacc[hh][mb][i4 * 4 + 3] * inv)};
+          *reinterpret_cast<u32x2_t*>(op + (size_t)rq * D + col) = pk;
+        }
+    }
   }
 }
 
@@ -300,11 +341,18 @@ bool prefill_bf16_supported(int D, int Dv) { return D == Dv && (D == 64 || D == 
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const int nQ = (a.Lq + kTile - 1) / kTile;
-  const dim3 grid((unsigned)((size_t)nQ * a.Hq * a.B));
-  if (a.D == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(kThreads), 0, s, a);
+  // heads per workgroup: two at D = 64 when the group size is even; at D = 128
+  // two heads' accumulators and Q operands no longer fit the register file
+  const int nh = (a.D == 64 && (a.Hq / a.Hkv) % 2 == 0) ? 2 : 1;
+  const dim3 grid((unsigned)((size_t)nQ * (a.Hq / nh) * a.B));
+  if (a.D == 64) {
+    if (nh == 2)
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, 2>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, 1>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, 1>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

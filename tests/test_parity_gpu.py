@@ -87,6 +87,8 @@ PREFILL_CASES = [
     ("lq_below_lk", 2, 2, 1, 700, 1300, 128, True, "diag_first", 9.0, 0.2),
     ("lq_above_lk", 1, 2, 2, 900, 400, 64, True, "ascending", 9.0, 0.1),
     ("noncausal_d64_diag", 1, 3, 1, 1000, 1000, 64, False, "diag_first", 9.0, 0.01),
+    ("d64_gqa_pairs", 2, 8, 2, 700, 900, 64, False, "ascending", 9.0, 0.05),
+    ("causal_gqa_group6", 1, 6, 1, 520, 520, 128, True, "diag_first", 9.0, 0.05),
     ("noncausal_ragged", 1, 2, 1, 513, 777, 128, False, "ascending", 9.0, 0.3),
     ("thr_above_one", 1, 2, 1, 513, 777, 128, False, "ascending", 3.0, 2.0),
     ("thr_one", 1, 2, 2, 640, 640, 128, True, "diag_first", 3.0, 1.0),
