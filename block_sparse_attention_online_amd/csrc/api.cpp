@@ -92,12 +92,17 @@ int chained_max_tiles(int D, int Dv, int group, bool latent) {
 }
 
 // Automatic split count: enough workgroups to keep all 256 compute units
-// streaming (4 resident workgroups each, 2 rounds), with no split longer than
-// a chained split may be.  Chained decisions do not depend on the count.
+// streaming (GQA: 4 resident workgroups each, 2 rounds; latent: one resident
+// workgroup each, 2 rounds, each sub-split taking one workgroup per 64 query
+// heads), with no split longer than a chained split may be.  Chained
+// decisions do not depend on the count.
 int auto_splits(int B, int Hq, int Hkv, int Lk, int D, int Dv, bool latent) {
   const int64_t nK = ceil_div(Lk, SS_TILE_KEYS);
   const int64_t units = (int64_t)B * Hkv;
-  const int64_t want = 2048;
+  const int group = Hq / Hkv;
+  const int64_t want = decode_kernel(D, Dv, group, latent) == DecodeKernel::kMla
+                           ? 512 / ssattn::decode_mla_workgroups_per_split(group)
+                           : 2048;
   int64_t per = ceil_div(nK * units, want);
   const int64_t cap = chained_max_tiles(D, Dv, Hq / Hkv, latent);
   if (per > cap) per = cap;
@@ -110,7 +115,7 @@ struct DecodePlan {
   int tiles_per_sub;   // tiles per sub-split
   int chain_tiles;     // tiles per chain
   int subs_per_chain;  // sub-splits per chain
-  size_t o_off, lse_off, slot_off, timeout_off, bytes;
+  size_t o_off, lse_off, slot_off, xchg_off, timeout_off, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -164,7 +169,13 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int Lk, int D, int Dv, bool laten
   p.o_off = 0;
   p.lse_off = align256(rows * (size_t)Dv * sizeof(float));
   p.slot_off = p.lse_off + align256(rows * sizeof(float));
-  p.timeout_off = p.slot_off + align256(slots * (size_t)(Hq / Hkv) * sizeof(unsigned long long));
+  p.xchg_off = p.slot_off + align256(slots * (size_t)(Hq / Hkv) * sizeof(unsigned long long));
+  // latent decode: the two halves of a head group exchange one value per tile
+  const size_t xchg = decode_kernel(D, Dv, Hq / Hkv, latent) == DecodeKernel::kMla
+                          ? slots * 2 * (size_t)ssattn::decode_mla_max_tiles(Hq / Hkv) *
+                                sizeof(unsigned long long)
+                          : 0;
+  p.timeout_off = p.xchg_off + align256(xchg);
   p.bytes = p.timeout_off + 256;
   return p;
 }
@@ -329,6 +340,8 @@ int prepare_decode(const ss_decode_params* p, bool stage_partial, ssattn::Decode
   a->part_o = reinterpret_cast<float*>(ws + pl.o_off);
   a->part_lse = reinterpret_cast<float*>(ws + pl.lse_off);
   a->lb_slot = reinterpret_cast<unsigned long long*>(ws + pl.slot_off);
+  a->lb_xchg = k == DecodeKernel::kMla ? reinterpret_cast<unsigned long long*>(ws + pl.xchg_off)
+                                       : nullptr;
   a->lb_timeouts = reinterpret_cast<unsigned int*>(ws + pl.timeout_off);
   a->B = p->B;
   a->Hq = p->Hq;

@@ -45,6 +45,8 @@ struct DecodeArgs {
   // earlier sub-splits of its chain before deciding.
   unsigned lb_tag;                 // nonzero, unique per launch (wraps after 2^31)
   unsigned long long* lb_slot;     // [S][B][Hkv][G] (tag << 32) | float bits
+  unsigned long long* lb_xchg;     // latent decode: [S][B][Hkv][2][64] per-tile statistic
+                                   // of each half of the head group (null otherwise)
   unsigned int* lb_timeouts;       // count of look-back waits that gave up
 };
 
@@ -59,6 +61,7 @@ int decode_gqa_max_tiles(int group);  // tiles a split may hold in chained mode
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
 bool decode_mla_supported(int D, int Dv, int group, bool latent);
 int decode_mla_max_tiles(int group);
+int decode_mla_workgroups_per_split(int group);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace ssattn

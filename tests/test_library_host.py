@@ -134,6 +134,14 @@ def test_split_policy_is_deterministic_and_bounded(ss):
         s = ss.ss_decode_num_splits(1, 4, 4, L, 128, 128)
         assert 1 <= s <= nK
     assert ss.ss_decode_num_splits(1, 3, 2, 100, 128, 128) == 0  # Hq % Hkv
+    # latent decode (576-wide rows, 512 value columns, one latent head): a
+    # sub-split runs as one workgroup per 64 query heads, 512 workgroups
+    # wanted, at most 64 tiles per sub-split
+    assert ss.ss_decode_num_splits(8, 128, 1, 16384, 576, 512) == 32   # 4 tiles each
+    assert ss.ss_decode_num_splits(8, 128, 1, 131072, 576, 512) == 32  # 32 tiles each
+    assert ss.ss_decode_num_splits(1, 128, 1, 1 << 20, 576, 512) == 256  # 32 tiles each
+    assert ss.ss_decode_num_splits(1, 128, 1, 1 << 23, 576, 512) == 1024  # capped at 64 tiles
+    assert ss.ss_decode_num_splits(2, 64, 1, 8192, 576, 512) == 64     # 1 tile each
 
 
 def test_workspace_bytes(ss):
@@ -152,6 +160,14 @@ def test_workspace_bytes(ss):
     assert n >= 3 * 4 * 128 * 4
     for args in [(16, 32, 8, 32768, 128, 128, 0), (2, 8, 2, 1000, 64, 64, 99)]:
         assert ss.ss_attn_decode_workspace_bytes(*args) > 0
+    # latent decode: split outputs, lse, per-row maxima, then the two halves'
+    # per-tile exchange ([sub-splits][B][2][64] 64-bit values)
+    S = 32  # B8 Hq128 Lk16384: 32 sub-splits of 4 tiles
+    o = S * 8 * 128 * 512 * 4
+    lse = S * 8 * 128 * 4
+    slots = S * 8 * 128 * 8
+    xchg = S * 8 * 2 * 64 * 8
+    assert ss.ss_attn_decode_workspace_bytes(8, 128, 1, 16384, 576, 512, 0) == o + lse + slots + xchg + 256
 
 
 # --------------------------------------------------------------------------- argument checks

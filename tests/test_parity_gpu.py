@@ -243,6 +243,39 @@ def test_decode_gqa_32k_full_size(ss, thr, mode):
     check_decode(ss, x, w.scale, thr, 0, pairs=pairs, name=w.name, mode=mode)
 
 
+MLA_CASES = [
+    # name, B, Hq, Lk, S, r, thr  (one latent head: D = 576, value = first 512 columns)
+    ("mla128_auto", 2, 128, 3000, 0, 9.0, 0.05),
+    ("mla64_splits", 1, 64, 2000, 3, 9.0, 0.1),
+    ("mla128_dense", 1, 128, 1500, 2, 3.0, 0.0),
+    ("mla128_thr1", 1, 128, 2500, 4, 9.0, 1.0),
+    ("mla128_thr_above_one", 1, 128, 1000, 2, 3.0, 2.0),
+    ("mla128_one_key", 1, 128, 1, 1, 3.0, 0.1),
+    ("mla128_many_splits", 1, 128, 2500, 99, 9.0, 0.05),
+    ("mla128_long_chain", 1, 128, 20000, 0, 9.0, 0.02),
+]
+
+
+@pytest.mark.parametrize("mode", ["chained", "independent"])
+@pytest.mark.parametrize("case", MLA_CASES, ids=[c[0] for c in MLA_CASES])
+def test_decode_mla_small(ss, case, mode):
+    name, B, Hq, Lk, S, r, thr = case
+    x = clustered_decode(zlib.crc32(name.encode()) % 10000, B, Hq, 1, Lk, 576, 512, 16, r,
+                         latent=True)
+    check_decode(ss, x, 1 / 24, thr, S, latent_dv=512, name=name, mode=mode)
+
+
+@pytest.mark.parametrize("thr,mode", [(0.0, "chained"), (0.3, "chained"), (0.5, "independent")])
+def test_decode_mla_16k_full_size(ss, thr, mode):
+    """Latent decode at full size (B8 Hq128 Lk16384, 576-wide latent rows,
+    value = first 512 columns) with the automatic split count; the oracle
+    checks three sampled batch entries."""
+    w = WORKLOADS["mla_decode_16k"]
+    x = make_inputs(w)
+    check_decode(ss, x, w.scale, thr, 0, pairs=[(0, 0), (3, 0), (7, 0)], latent_dv=512,
+                 name=w.name, mode=mode)
+
+
 # --------------------------------------------------------------------------- determinism
 
 def test_repeat_runs_are_bitwise_identical(ss):
