@@ -60,8 +60,18 @@ constexpr int kSpinCap = 1 << 21;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// Physical 16-byte chunk of logical chunk c in row r of a slot.
-__device__ __forceinline__ int slot_chunk(int r, int c) { return c ^ (r & 7); }
+// Physical 16-byte chunk of logical chunk c in row r of a ring step, per
+// step kind, so that each kind's operand reads hit 16 different chunk
+// positions (all banks) per 16 lanes:
+//  * score step, 128 columns (16 chunks, 256-byte rows): 16 consecutive rows
+//    read the same logical chunk -> c ^ (r & 15);
+//  * score step, 64 columns (8 chunks, 128-byte rows, two rows per 256
+//    bytes) -> c ^ ((r >> 1) & 7);
+//  * value step (transpose reads: 4 consecutive rows x 2 adjacent chunks
+//    per 16 lanes) -> c ^ ((r & 7) << 1).
+__device__ __forceinline__ int swz_score128(int r) { return r & 15; }
+__device__ __forceinline__ int swz_score64(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_value(int r) { return (r & 7) << 1; }
 
 // s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding).
 template <int N>
@@ -117,6 +127,7 @@ struct ScorePlan {  // score pass: all 576 columns
   static constexpr int P = 6;
   static constexpr int col[P] = {0, 128, 256, 384, 448, 512};
   static constexpr int width[P] = {128, 128, 128, 64, 64, 64};
+  static constexpr bool value[P] = {false, false, false, false, false, false};
 };
 struct KeptPlan {  // kept tile: 576 score columns, then the 512 value columns again
   static constexpr int P = 9;
@@ -168,7 +179,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  // wave index as a scalar: everything derived from it (ring destinations,
+  // row bases) stays in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int q = lane >> 4;                   // MFMA k-group of this lane
   const int head0 = hk * G + half * kHalf;   // first query head of this half
@@ -214,11 +227,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
   };
 
   // A step holds W = 128 or 64 columns from column C of the tile's 128 keys:
-  // rows of 2 W bytes, logical 16-byte chunk c of row r at chunk c ^ (r & 7).
+  // rows of 2 W bytes, 16-byte chunks swizzled by the step kind's rule above.
   // Wave w loads rows [32 w, 32 w + 32), 1024 bytes per instruction.  Keys
   // past Lk read the last key row (their scores are masked, their p is 0).
-  auto issue = [&](auto C_, auto W_, int tile, unsigned char* dst) __attribute__((always_inline)) {
+  auto issue = [&](auto C_, auto W_, auto V_, int tile, unsigned char* dst)
+                   __attribute__((always_inline)) {
     constexpr int C = decltype(C_)::value, W = decltype(W_)::value;
+    constexpr bool V = decltype(V_)::value;
     constexpr int CPR = W / 8;         // chunks per row
     constexpr int RPI = 64 / CPR;      // rows per instruction
     constexpr int NI = 32 / RPI;       // instructions per wave
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
     for (int i = 0; i < NI; ++i) {
       const int r = (w * NI + i) * RPI + lr;
       const int key = min(tile * kTile + r, a.Lk - 1);
-      const int lc = pc ^ (r & 7);
+      const int lc = pc ^ (V ? swz_value(r) : (W == 128 ? swz_score128(r) : swz_score64(r)));
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)(kp + (size_t)key * kDqk + C + lc * 8),
           (void __attribute__((address_space(3)))*)(dst + (w * NI + i) * 1024), 16, 0, 0);
@@ -238,8 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
   // lane holds head l16, keys 16 kb + 4 q + i
   f32x4_t sacc[8];
   // scores over the step's columns: k-step ks (32 columns) reads logical
-  // chunk 4 ks + q of row 16 kb + l16; the chunk index bits above the swizzle
-  // (ks >> 1) and the row block (kb) become immediate offsets
+  // chunk 4 ks + q of row 16 kb + l16
   auto score = [&](auto C_, auto W_, const unsigned char* sl) __attribute__((always_inline)) {
     constexpr int C = decltype(C_)::value, W = decltype(W_)::value;
     constexpr int NKS = W / 32;
@@ -247,18 +261,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const int sw = l16 & 7;
+    // rows 16 kb + l16: the swizzle depends on l16 only, the row block is an
+    // immediate offset
+    const int sw = W == 128 ? swz_score128(l16) : swz_score64(l16);
     const unsigned char* base = sl + l16 * (2 * W);
+    auto read = [&](int ks, u32x4_t (&kv)[8]) __attribute__((always_inline)) {
+      const int off = ((4 * ks + q) ^ sw) << 4;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+        kv[kb] = *reinterpret_cast<const u32x4_t*>(base + kb * 16 * (2 * W) + off);
+    };
+    // operands of k-step ks + 1 are read while the MFMAs of k-step ks run
+    u32x4_t kv[2][8];
+    read(0, kv[0]);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const int off = (((4 * (ks & 1) + q) ^ sw) << 4) + (ks >> 1) * 128;
+      if (ks + 1 < NKS) read(ks + 1, kv[(ks + 1) & 1]);
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(base + kb * 16 * (2 * W) + off);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qf[C / 32 + ks],
-                                                          sacc[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 8; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks & 1][kb]),
+                                                          qf[C / 32 + ks], sacc[kb], 0, 0, 0);
     }
+    // schedule: the first k-step's reads, then one MFMA per read of the next
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 8 * (NKS - 1); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   // scores of the tile in log2 units, keys past Lk at -inf; returns the tile
@@ -290,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
     auto load = [&](int t, auto E, unsigned char* dst) __attribute__((always_inline)) {
       constexpr int e = decltype(E)::value;
       issue(std::integral_constant<int, PL::col[e]>{}, std::integral_constant<int, PL::width[e]>{},
-            tile_of(min(t, nt - 1)), dst);
+            std::integral_constant<bool, PL::value[e]>{}, tile_of(min(t, nt - 1)), dst);
     };
     load(0, std::integral_constant<int, 0>{}, slot0);
     load(0, std::integral_constant<int, 1>{}, slot1);
@@ -444,28 +475,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
       // 32-key step j: rows 32 j + 4 q + (l16 >> 2) and + 16 (the keys of P's
       // k-elements), 4 columns from 4 (l16 & 3) of the block.
       const int rr = q * 4 + (l16 >> 2);  // row within the 16-key block
-      const int sw = rr & 7;
+      const int sw = swz_value(rr);       // rows 32 j + rr and + 16 share it
       const int cq = (l16 & 3) * 4;       // first of the lane's 4 columns
       const unsigned char* base = sl + rr * 256 + (cq & 7) * 2;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8_t pb = as_bf16x8(u32x4_t{pw[j][0], pw[j][1], pw[j][2], pw[j][3]});
+      auto read = [&](int j, u32x4_t (&vv)[8]) __attribute__((always_inline)) {
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
-          // chunk (2 cb + cq / 8) ^ sw; cb's bit 2 sits above the swizzle
-          const int off = (((2 * (cb & 3) + (cq >> 3)) ^ sw) << 4) + (cb >> 2) * 128;
+          const int off = ((2 * cb + (cq >> 3)) ^ sw) << 4;
           const s16x4_t lo =
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + 32 * j * 256 + off));
           const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_s16x4_t*)(base + (32 * j + 16) * 256 + off));
           const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
           const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
-          const u32x4_t vv = {l2[0], l2[1], h2[0], h2[1]};
+          vv[cb] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+        }
+      };
+      // V^T operands of 32-key step j + 1 are read while the MFMAs of step j run
+      u32x4_t vv[2][8];
+      read(0, vv[0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j + 1 < 4) read(j + 1, vv[(j + 1) & 1]);
+        const bf16x8_t pb = as_bf16x8(u32x4_t{pw[j][0], pw[j][1], pw[j][2], pw[j][3]});
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
           constexpr int ob = C / 16;
-          oacc[ob + cb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), pb, oacc[ob + cb], 0, 0, 0);
+          oacc[ob + cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv[j & 1][cb]), pb,
+                                                                 oacc[ob + cb], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
   };
   if (nkept > 0)
