@@ -1,0 +1,397 @@
+"""Per-workload measurement runs of the skip-softmax hot path on one GPU.
+
+  python -m block_sparse_attention_online_amd.harness prefill [--out FILE]
+      causal GQA prefill (B1, Hq32/Hkv8, L16384, D128): skip targets
+      0.1 .. 0.8 found by bisection on the kernel's own mask, both visit
+      orders, the literal generator (r = 3) and the wide-gap one (r = 9):
+      executed TFLOP/s, speedup over threshold 0, error against threshold 0.
+  python -m block_sparse_attention_online_amd.harness video [--out FILE]
+      video-DiT self-attention (B1, H24, 13x42x60 tokens, D128): the
+      calibrated factor a*exp(b*s) fitted on replicate 1 and evaluated on
+      replicate 0 at s = 0.5, 0.7, 0.9; timestep gating t = 1.0, 0.6, 0.2 with
+      the dense-until point 0.7.
+  python -m block_sparse_attention_online_amd.harness latent [--out FILE]
+      latent decode (B8, 128 heads, 576-wide latent rows, value = first 512
+      columns) at 16K..128K keys: one factor a*exp(0.7 b) fitted so ~70 % of
+      tiles skip at every length; K bytes per second and MFMA rate.
+  python -m block_sparse_attention_online_amd.harness decode [--out FILE]
+      GQA decode (B16, Hq32/Hkv8, 32768 keys, D128): skip 0.5 / 0.7 / 0.9
+      against threshold 0, chained splits.
+
+The method and its parameters: vLLM-Omni design page "Skip-Softmax",
+sections "The threshold" and "Timestep gating"; BLASST summary page, section
+"Calibratie en Thresholding" (threshold = a / L with a fitted so the
+sparsity stays fixed across context lengths).
+
+Every timed call is preceded by a rewrite of a 1 GiB buffer, so no call
+finds its K/V in L2 or in the 256 MB last-level cache; times are the median
+of the per-call HIP event times on the current stream.  Each run prints one
+JSON object per measured point; --out also writes a markdown table.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from . import (lib, mask_shape_decode, mask_shape_prefill, ss_attn_decode_partial,
+               ss_attn_decode_combine, ss_attn_decode_workspace_bytes, ss_attn_prefill_ex,
+               ss_decode_num_splits, ss_resolve_threshold)
+from .calibrate import bisect_threshold, fit_factor, skip_fraction
+
+BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Median per-call time in ms, with L2 and last-level cache evicted
+    before every call."""
+
+    def __init__(self, flush_bytes: int = 1 << 30):
+        self.flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+
+    def ms(self, fn, iters: int = 15, warmup: int = 3) -> float:
+        for _ in range(warmup):
+            fn()
+        ts = []
+        for i in range(iters):
+            self.flush.fill_(i & 255)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+
+def rel_l2_gpu(a: torch.Tensor, b: torch.Tensor) -> float:
+    a, b = a.float(), b.float()
+    return float(torch.linalg.norm(a - b) / torch.linalg.norm(b))
+
+
+def md_table(rows, cols) -> str:
+    out = ["| " + " | ".join(cols) + " |", "|" + "---|" * len(cols)]
+    for r in rows:
+        out.append("| " + " | ".join(str(r.get(c, "")) for c in cols) + " |")
+    return "\n".join(out)
+
+
+def emit(rec, rows):
+    print(json.dumps(rec), flush=True)
+    rows.append(rec)
+
+
+# --------------------------------------------------------------------------- prefill
+
+def prefill_flops(mask_np, D, Dv):
+    """Executed MFMA flops: Q.K^T of every visited (query tile, key tile),
+    P.V of the kept ones, full 128 x 128 tiles as issued."""
+    visited = int((mask_np != 2).sum())
+    kept = int((mask_np == 0).sum())
+    return 2 * 128 * 128 * D * visited + 2 * 128 * 128 * Dv * kept
+
+
+def run_prefill_sweep(args):
+    from synth import WORKLOADS, make_inputs
+
+    timer, rows = Timer(), []
+    targets = [0.1 * i for i in range(1, 9)]
+    for r in (3.0, 9.0):
+        w = WORKLOADS["gqa_prefill_16k"].replace(r=r)
+        x = make_inputs(w)
+        q, k, v = (x[n].cuda() for n in "qkv")
+        del x
+        out = torch.empty_like(q)
+        mask = torch.empty(mask_shape_prefill(w.B, w.Hq, w.Lq, w.Lk), dtype=torch.uint8,
+                           device="cuda")
+        fa = 4.0 * w.B * w.Hq * w.Lq * w.Lk * w.D * 0.5
+        for order in ("ascending", "diag_first"):
+            def run(thr):
+                ss_attn_prefill_ex(q, k, v, out, scale=w.scale, causal=True, threshold=thr,
+                                   skip_mask=mask, order=order)
+
+            def skip_at(thr):
+                run(thr)
+                torch.cuda.synchronize()
+                return skip_fraction(mask)
+
+            dense_ms = timer.ms(lambda: run(0.0))
+            dense_out = out.clone()
+            dense_fl = prefill_flops(mask.cpu().numpy(), w.D, w.Dv)
+            emit({"workload": "gqa_prefill_16k", "r": r, "order": order, "target": 0.0,
+                  "threshold": 0.0, "skip": 0.0, "ms": round(dense_ms, 4),
+                  "tflops_executed": round(dense_fl / dense_ms / 1e9, 1),
+                  "frac_bf16_peak": round(dense_fl / dense_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                  "fa_tflops": round(fa / dense_ms / 1e9, 1), "speedup": 1.0,
+                  "rel_l2_vs_dense": 0.0}, rows)
+            for tgt in targets:
+                thr, s, reach = bisect_threshold(skip_at, tgt, iters=24, tol=0.005)
+                ms = timer.ms(lambda: run(thr))
+                fl = prefill_flops(mask.cpu().numpy(), w.D, w.Dv)
+                emit({"workload": "gqa_prefill_16k", "r": r, "order": order,
+                      "target": round(tgt, 2), "threshold": float(f"{thr:.6g}"),
+                      "reachable": reach, "skip": round(skip_fraction(mask), 4),
+                      "ms": round(ms, 4), "tflops_executed": round(fl / ms / 1e9, 1),
+                      "frac_bf16_peak": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                      "fa_tflops": round(fa / ms / 1e9, 1),
+                      "speedup": round(dense_ms / ms, 3),
+                      "rel_l2_vs_dense": float(f"{rel_l2_gpu(out, dense_out):.3e}")}, rows)
+        del q, k, v, out
+    cols = ["r", "order", "target", "threshold", "reachable", "skip", "ms", "tflops_executed",
+            "frac_bf16_peak", "fa_tflops", "speedup", "rel_l2_vs_dense"]
+    return rows, cols
+
+
+# --------------------------------------------------------------------------- video
+
+def run_video(args):
+    from synth import WORKLOADS, make_inputs
+
+    timer, rows = Timer(), []
+    w = WORKLOADS["video_dit_32760"]
+    L = w.Lk
+    fa = 4.0 * w.B * w.Hq * w.Lq * w.Lk * w.D
+    grid = [float(f"{t:.3g}") for t in np.logspace(-6, 0, 13)]
+
+    def load(seed):
+        t = time.time()
+        x = make_inputs(w.replace(seed=seed))
+        log(f"[video] generated seed {seed} in {time.time() - t:.1f}s")
+        return tuple(x[n].cuda() for n in "qkv")
+
+    out = mask = None
+    fits = {}
+    # 1. calibration sweep on replicate 1
+    q, k, v = load(w.seed + 1)
+    out = torch.empty_like(q)
+    mask = torch.empty(mask_shape_prefill(w.B, w.Hq, w.Lq, w.Lk), dtype=torch.uint8,
+                       device="cuda")
+    for order in ("ascending", "diag_first"):
+        pts = []
+        for thr in grid:
+            ss_attn_prefill_ex(q, k, v, out, scale=w.scale, causal=False, threshold=thr,
+                               skip_mask=mask, order=order)
+            torch.cuda.synchronize()
+            s = skip_fraction(mask)
+            emit({"workload": w.name, "replicate": 1, "stage": "sweep", "order": order,
+                  "threshold": thr, "skip": round(s, 4)}, rows)
+            if 0.02 < s < 0.98:
+                pts.append((thr, L, s))
+        a, b = fit_factor(pts) if len(pts) >= 2 else (float("nan"), float("nan"))
+        fits[order] = (a, b)
+        emit({"workload": w.name, "replicate": 1, "stage": "fit", "order": order,
+              "a": float(f"{a:.6g}"), "b": float(f"{b:.6g}"), "points": len(pts)}, rows)
+    del q, k, v
+    # 2. evaluation on replicate 0
+    q, k, v = load(w.seed)
+    for order in ("ascending", "diag_first"):
+        a, b = fits[order]
+
+        def run(thr):
+            ss_attn_prefill_ex(q, k, v, out, scale=w.scale, causal=False, threshold=thr,
+                               skip_mask=mask, order=order)
+
+        dense_ms = timer.ms(lambda: run(0.0), iters=9)
+        dense_out = out.clone()
+        emit({"workload": w.name, "replicate": 0, "stage": "dense", "order": order,
+              "ms": round(dense_ms, 3), "fa_tflops": round(fa / dense_ms / 1e9, 1)}, rows)
+        if not math.isfinite(a):
+            continue
+        for tgt in (0.5, 0.7, 0.9):
+            thr = ss_resolve_threshold("calibrated", a=a, b=b, target_sparsity=tgt, seqlen=L)
+            ms = timer.ms(lambda: run(thr), iters=9)
+            fl = prefill_flops(mask.cpu().numpy(), w.D, w.Dv)
+            emit({"workload": w.name, "replicate": 0, "stage": "calibrated", "order": order,
+                  "target": tgt, "threshold": float(f"{thr:.6g}"),
+                  "skip": round(skip_fraction(mask), 4), "ms": round(ms, 3),
+                  "tflops_executed": round(fl / ms / 1e9, 1),
+                  "frac_bf16_peak": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                  "speedup": round(dense_ms / ms, 3),
+                  "rel_l2_vs_dense": float(f"{rel_l2_gpu(out, dense_out):.3e}")}, rows)
+        for t in (1.0, 0.6, 0.2):
+            thr = ss_resolve_threshold("calibrated", a=a, b=b, target_sparsity=0.7, seqlen=L,
+                                       timestep=t, disabled_until=0.7)
+            ms = timer.ms(lambda: run(thr), iters=9)
+            emit({"workload": w.name, "replicate": 0, "stage": "gating", "order": order,
+                  "timestep": t, "disabled_until": 0.7, "mode": "dense" if thr == 0 else "sparse",
+                  "threshold": float(f"{thr:.6g}"), "skip": round(skip_fraction(mask), 4),
+                  "ms": round(ms, 3)}, rows)
+    cols = ["replicate", "stage", "order", "threshold", "a", "b", "target", "timestep", "mode",
+            "skip", "ms", "tflops_executed", "frac_bf16_peak", "fa_tflops", "speedup",
+            "rel_l2_vs_dense"]
+    return rows, cols
+
+
+# --------------------------------------------------------------------------- latent decode
+
+def run_latent(args):
+    from synth import WORKLOADS, make_inputs
+
+    timer, rows = Timer(), []
+    ctxs = [16, 32, 64, 128]
+    grid = [float(f"{t:.3g}") for t in np.logspace(-5, 0, 11)]
+    for r in (3.0, 9.0):
+        data, pts, per_ctx = {}, [], {}
+        for n in ctxs:
+            w = WORKLOADS[f"mla_decode_{n}k"].replace(r=r)
+            x = make_inputs(w)
+            q, k = x["q"].cuda(), x["k"].cuda()
+            del x
+            ws = torch.empty(ss_attn_decode_workspace_bytes(w.B, w.Hq, 1, w.Lk, 576, 512, 0),
+                             dtype=torch.uint8, device="cuda")
+            mask = torch.empty(mask_shape_decode(w.B, 1, w.Lk), dtype=torch.uint8, device="cuda")
+            out = torch.empty((w.B, w.Hq, 512), dtype=torch.bfloat16, device="cuda")
+
+            def part(thr, q=q, k=k, ws=ws, mask=mask, w=w):
+                ss_attn_decode_partial(q, k, None, dv=512, scale=w.scale, threshold=thr,
+                                       skip_mask=mask, workspace=ws)
+
+            def call(thr, part=part, q=q, k=k, ws=ws, out=out):
+                part(thr)
+                ss_attn_decode_combine(q, k, ws, out, dv=512)
+
+            def skip_at(thr, part=part, mask=mask):
+                part(thr)
+                torch.cuda.synchronize()
+                return skip_fraction(mask)
+
+            for thr in grid:
+                s = skip_at(thr)
+                if 0.02 < s < 0.98:
+                    pts.append((thr, w.Lk, s))
+            t70, s70, reach = bisect_threshold(skip_at, 0.7, iters=24, tol=0.005)
+            per_ctx[n] = (t70, s70, reach)
+            data[n] = (w, call, skip_at, mask, out, q, k, ws)
+        a_fit, b = fit_factor(pts) if len(pts) >= 2 else (float("nan"), 0.0)
+        # one a for all lengths: ln a = mean over lengths of ln(t70 * L) - 0.7 b
+        la = [math.log(per_ctx[n][0] * data[n][0].Lk) - 0.7 * b for n in ctxs if per_ctx[n][2]]
+        a = math.exp(sum(la) / len(la)) if la else float("nan")
+        emit({"workload": "mla_decode", "r": r, "stage": "fit", "b": float(f"{b:.6g}"),
+              "a_sweep": float(f"{a_fit:.6g}"), "a_70": float(f"{a:.6g}"),
+              "contexts_reaching_0.7_at_thr_le_1": [n for n in ctxs if per_ctx[n][2]]}, rows)
+        for n in ctxs:
+            w, call, skip_at, mask, out, q, k, ws = data[n]
+            kbytes = w.B * w.Lk * 576 * 2
+            dense_ms = timer.ms(lambda: call(0.0))
+            dense_out = out.clone()
+            cases = [("bisected", per_ctx[n][0])]
+            if math.isfinite(a):
+                cases.append(("calibrated", ss_resolve_threshold(
+                    "calibrated", a=a, b=b, target_sparsity=0.7, seqlen=w.Lk)))
+            emit({"workload": f"mla_decode_{n}k", "r": r, "stage": "dense",
+                  "ms": round(dense_ms, 4), "k_gbs": round(kbytes / dense_ms / 1e6, 1),
+                  "frac_hbm": round(kbytes / dense_ms / 1e6 / HBM_PEAK_GBS, 4)}, rows)
+            for kind, thr in cases:
+                ms = timer.ms(lambda: call(thr))
+                s = skip_at(thr)
+                call(thr)
+                torch.cuda.synchronize()
+                m = mask.cpu().numpy()
+                keys = np.full(m.shape[-1], 128)
+                keys[-1] = w.Lk - 128 * (m.shape[-1] - 1)
+                kept_keys = int(((m == 0) * keys[None, None, :]).sum())
+                flops = 2.0 * w.Hq * (w.B * w.Lk * 576 + kept_keys * 512)
+                emit({"workload": f"mla_decode_{n}k", "r": r, "stage": kind,
+                      "threshold": float(f"{thr:.6g}"),
+                      "reachable": per_ctx[n][2] if kind == "bisected" else None,
+                      "skip": round(s, 4), "ms": round(ms, 4),
+                      "k_gbs": round(kbytes / ms / 1e6, 1),
+                      "frac_hbm": round(kbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                      "mfma_tflops": round(flops / ms / 1e9, 1),
+                      "frac_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                      "speedup": round(dense_ms / ms, 3),
+                      "rel_l2_vs_dense": float(f"{rel_l2_gpu(out, dense_out):.3e}")}, rows)
+        del data
+        torch.cuda.empty_cache()
+    cols = ["workload", "r", "stage", "threshold", "b", "a_70", "reachable", "skip", "ms",
+            "k_gbs", "frac_hbm", "mfma_tflops", "frac_bf16_peak", "speedup", "rel_l2_vs_dense"]
+    return rows, cols
+
+
+# --------------------------------------------------------------------------- GQA decode
+
+def run_decode(args):
+    from synth import WORKLOADS, make_inputs
+
+    timer, rows = Timer(), []
+    w = WORKLOADS["gqa_decode_32k"]
+    x = make_inputs(w)
+    q, k, v = (x[n].cuda() for n in "qkv")
+    del x
+    ws = torch.empty(ss_attn_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lk, w.D, w.Dv, 0),
+                     dtype=torch.uint8, device="cuda")
+    mask = torch.empty(mask_shape_decode(w.B, w.Hkv, w.Lk), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda")
+
+    def part(thr):
+        ss_attn_decode_partial(q, k, v, scale=w.scale, threshold=thr, skip_mask=mask,
+                               workspace=ws)
+
+    def call(thr):
+        part(thr)
+        ss_attn_decode_combine(q, k, ws, out, v=v)
+
+    def skip_at(thr):
+        part(thr)
+        torch.cuda.synchronize()
+        return skip_fraction(mask)
+
+    kb = w.B * w.Hkv * w.Lk * w.D * 2
+    dense_ms = timer.ms(lambda: call(0.0))
+    dense_out = out.clone()
+    emit({"workload": w.name, "target": 0.0, "threshold": 0.0, "skip": 0.0,
+          "ms": round(dense_ms, 4), "gbs": round(2 * kb / dense_ms / 1e6, 1), "speedup": 1.0},
+         rows)
+    for tgt in (0.5, 0.7, 0.9):
+        thr, s, reach = bisect_threshold(skip_at, tgt)
+        ms = timer.ms(lambda: call(thr))
+        s = skip_at(thr)
+        by = kb * (1 + (1 - s))
+        emit({"workload": w.name, "target": tgt, "threshold": float(f"{thr:.6g}"),
+              "reachable": reach, "skip": round(s, 4), "ms": round(ms, 4),
+              "gbs": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / HBM_PEAK_GBS, 4),
+              "speedup": round(dense_ms / ms, 3),
+              "rel_l2_vs_dense": float(f"{rel_l2_gpu(out, dense_out):.3e}")}, rows)
+    cols = ["target", "threshold", "reachable", "skip", "ms", "gbs", "frac_hbm", "speedup",
+            "rel_l2_vs_dense"]
+    return rows, cols
+
+
+RUNS = {"prefill": run_prefill_sweep, "video": run_video, "latent": run_latent,
+        "decode": run_decode}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("run", choices=sorted(RUNS))
+    ap.add_argument("--out", default=None, help="also write a markdown table here")
+    args = ap.parse_args(argv)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    lib()
+    t = time.time()
+    rows, cols = RUNS[args.run](args)
+    log(f"[{args.run}] done in {time.time() - t:.1f}s")
+    if args.out:
+        cmd = "python -m block_sparse_attention_online_amd.harness " + " ".join(
+            argv if argv is not None else sys.argv[1:])
+        with open(args.out, "w") as f:
+            f.write(f"# {args.run}\n\nCommand: `{cmd}`\n\n{md_table(rows, cols)}\n")
+
+
+if __name__ == "__main__":
+    main()
