@@ -14,9 +14,15 @@ decode's algorithmic bytes (K, plus V of the kept tiles, plus q and out) per
 second of step wall time.  The causal GQA prefill (B1, Hq32/Hkv8, L16384,
 D128) is timed in the same run and reported under ``prefill``.
 
-``roofline`` is for the decode kernel alone, timed with HIP events on the
-stream it is launched on; ``cpu_baseline`` times the fp64 CPU oracle on a
-bounded sample of the same decode.
+Every timed step is preceded by a rewrite of a 1 GiB buffer, so no step finds
+K/V in L2 or in the 256 MB last-level cache; the step and its kernels are
+timed with HIP events on the stream they run on, and ``value`` uses the mean
+of those step times.  ``warm_value`` is the same decode run back to back
+(wall clock over the steps, caches left as the previous step left them).
+
+``roofline`` is for the decode kernel alone; ``cpu_baseline`` times the fp64
+CPU oracle on a bounded sample of the same decode.  ``latent`` is the
+latent-cache decode (B8, 128 heads, 576-wide rows, 131072 keys).
 
 Usage: python bench.py [--steps K] [--warmup W] [--target-skip 0.7]
        python bench.py --copy-probe       (a plain 1 GiB device copy, for
@@ -107,35 +113,45 @@ def bench_decode(ss, torch, args):
     log(f"[decode] threshold {thr:.6g} (reachable={reachable}) splits={S}")
 
     def timed(th, steps, warmup):
+        """(step ms, decode kernel ms, combine ms) over `steps` cold steps, each
+        after a cache-evicting rewrite; plus the warm wall-clock step ms."""
         for _ in range(warmup):
             partial(th)
             combine()
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        t0 = time.perf_counter()
-        for e in evs:
+        for i, e in enumerate(evs):
+            args.flush.fill_(i & 255)
             e[0].record()
             partial(th)
             e[1].record()
             combine()
             e[2].record()
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / steps
+        step = sum(e[0].elapsed_time(e[2]) for e in evs) / steps
         kern = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
         comb = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-        return wall, kern, comb
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            partial(th)
+            combine()
+        torch.cuda.synchronize()
+        warm = (time.perf_counter() - t0) * 1e3 / steps
+        return step, kern, comb, warm
 
     res = {"workload": w, "S": S, "thr": thr, "reachable": reachable, "x": x}
     if not args.only_sparse_decode:
         res["dense"] = timed(0.0, args.steps, args.warmup)
-        log(f"[decode] dense: step {res['dense'][0]:.4f} ms, kernel {res['dense'][1]:.4f} ms")
+        log(f"[decode] dense: step {res['dense'][0]:.4f} ms, kernel {res['dense'][1]:.4f} ms, "
+            f"warm step {res['dense'][3]:.4f} ms")
     res["sparse"] = timed(thr, args.steps, args.warmup)
     torch.cuda.synchronize()
     res["mask"] = mask.cpu().numpy()
     res["skip"] = skip_fraction(mask)
     res["bytes"] = decode_bytes(res["mask"], B, Hq, Hkv, Lk, D, Dv, S)
     log(f"[decode] sparse: step {res['sparse'][0]:.4f} ms, kernel {res['sparse'][1]:.4f} ms, "
-        f"combine {res['sparse'][2]:.4f} ms, skip {res['skip']:.3f}")
+        f"combine {res['sparse'][2]:.4f} ms, warm step {res['sparse'][3]:.4f} ms, "
+        f"skip {res['skip']:.3f}")
     return res
 
 
@@ -169,20 +185,24 @@ def bench_prefill(ss, torch, args, r, order):
         torch.cuda.synchronize()
         return skip_fraction(mask)
 
-    thr, s, reachable = bisect_threshold(skip_at, args.target_skip, iters=20, tol=0.01)
+    if args.prefill_threshold is not None:
+        thr, reachable = args.prefill_threshold, True
+    else:
+        thr, s, reachable = bisect_threshold(skip_at, args.target_skip, iters=20, tol=0.01)
 
     def timed(th):
         for _ in range(max(2, args.warmup // 2)):
             run(th)
         torch.cuda.synchronize()
         steps = max(5, args.steps // 2)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i, e in enumerate(evs):
+            args.flush.fill_(i & 255)
+            e[0].record()
             run(th)
-        e1.record()
+            e[1].record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
         return ms, mask.cpu().numpy()
 
     dense_ms, dmask = timed(0.0)
@@ -200,6 +220,61 @@ def bench_prefill(ss, torch, args, r, order):
            "frac_of_bf16_peak": round(fl_s / sparse_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
            "fa_convention_tflops": round(fa / sparse_ms / 1e9, 2)}
     log(f"[prefill r={r} {order}] {res}")
+    return res
+
+
+# --------------------------------------------------------------------------- latent decode
+
+def bench_latent(ss, torch, args):
+    """Latent-cache decode at 131072 keys: threshold 0 against the threshold
+    calibrated to the target skip (chained splits); K bytes per second."""
+    from block_sparse_attention_online_amd.calibrate import bisect_threshold, skip_fraction
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS["mla_decode_128k"]
+    x = make_inputs(w)
+    q, k = x["q"].cuda(), x["k"].cuda()
+    del x
+    ws = torch.empty(ss.ss_attn_decode_workspace_bytes(w.B, w.Hq, 1, w.Lk, 576, 512, 0),
+                     dtype=torch.uint8, device="cuda")
+    mask = torch.empty(ss.mask_shape_decode(w.B, 1, w.Lk), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.B, w.Hq, 512), dtype=torch.bfloat16, device="cuda")
+
+    def call(thr):
+        ss.ss_attn_decode_partial(q, k, None, dv=512, scale=w.scale, threshold=thr,
+                                  skip_mask=mask, workspace=ws)
+        ss.ss_attn_decode_combine(q, k, ws, out, dv=512)
+
+    def skip_at(thr):
+        call(thr)
+        torch.cuda.synchronize()
+        return skip_fraction(mask)
+
+    thr, _, reachable = bisect_threshold(skip_at, args.target_skip, iters=24, tol=0.005)
+
+    def timed(th):
+        for _ in range(3):
+            call(th)
+        steps = max(5, args.steps // 4)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i, e in enumerate(evs):
+            args.flush.fill_(i & 255)
+            e[0].record()
+            call(th)
+            e[1].record()
+        torch.cuda.synchronize()
+        return sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+
+    dense_ms = timed(0.0)
+    ms = timed(thr)
+    s = skip_at(thr)
+    kbytes = w.B * w.Lk * 576 * 2
+    res = {"workload": f"{w.name} (B8 Hq128, one 576-wide latent head, value = first 512 "
+                       "columns)", "threshold": thr, "threshold_reaches_target": reachable,
+           "skip_fraction": round(s, 4), "ms": round(ms, 4), "dense_ms": round(dense_ms, 4),
+           "k_gbs": round(kbytes / ms / 1e6, 1), "dense_k_gbs": round(kbytes / dense_ms / 1e6, 1),
+           "speedup_vs_dense": round(dense_ms / ms, 3)}
+    log(f"[latent] {res}")
     return res
 
 
@@ -268,7 +343,10 @@ def main():
     ap.add_argument("--target-skip", type=float, default=0.70)
     ap.add_argument("--threshold", type=float, default=None,
                     help="use this decode threshold instead of calibrating")
+    ap.add_argument("--prefill-threshold", type=float, default=None,
+                    help="use this prefill threshold instead of calibrating")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-latent", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only-sparse-decode", action="store_true",
                     help="time only the sparse decode (for hardware-counter runs)")
@@ -290,11 +368,12 @@ def main():
         copy_probe(torch)
         return
     if args.only_sparse_decode:
-        args.no_prefill = args.no_cpu = True
+        args.no_prefill = args.no_cpu = args.no_latent = True
+    args.flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
     dec = bench_decode(ss, torch, args)
     w, by = dec["workload"], dec["bytes"]
-    wall, kern, comb = dec["sparse"]
+    wall, kern, comb, warm = dec["sparse"]
     step_bytes = by["k"] + by["v_kept"] + by["q"] + by["out"]
     kern_bytes = by["k"] + by["v_kept"] + by["q"] + by["partials"]
     achieved = kern_bytes / (kern * 1e-3) / 1e9
@@ -309,6 +388,8 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall, 4),
+        "warm_value": round(step_bytes / (warm * 1e-3) / 1e9, 1),
+        "warm_ms_per_step": round(warm, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
@@ -320,7 +401,7 @@ def main():
         "roofline": roof,
     }
     if "dense" in dec:
-        dwall, dkern, _ = dec["dense"]
+        dwall, dkern, _, dwarm = dec["dense"]
         line["speedup_vs_dense"] = round(dwall / wall, 3)
         line["dense_ms_per_step"] = round(dwall, 4)
         dense_bytes = by["k"] + by["v_dense"] + by["q"] + by["out"]
@@ -329,6 +410,8 @@ def main():
         line["prefill"] = {"workload": "gqa_prefill_16k (B1 Hq32 Hkv8 L16384 D128 causal)",
                            "literal": bench_prefill(ss, torch, args, 3.0, "diag_first"),
                            "wide_gap": bench_prefill(ss, torch, args, 9.0, "diag_first")}
+    if not args.no_latent:
+        line["latent"] = bench_latent(ss, torch, args)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
     print(json.dumps(line), flush=True)
