@@ -22,8 +22,12 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssattn.so")
 ARCH = "gfx950"
 
-# Packed fp32 instructions are kept out of every device build.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 instructions are kept out of every device build.  MFMA results
+# stay in VGPRs (the MFMA's VGPR form): the score accumulators feed vector ALU
+# work (max, exp), and in AGPRs every such use costs a v_accvgpr_read and
+# every rescale a read and a write.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 

@@ -187,13 +187,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
       // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 rows (K operands read from
       // LDS just before each block's MFMAs)
       f32x16_t sacc[4];
+      // row kb * 32 + l32, logical chunk 2 ks + g: the swizzle sees only
+      // l32 & 7 and chunk bits 0..2, so four per-lane offsets cover every k-step
+      // (bit 3 of the chunk and the row block are immediate offsets)
+      const unsigned char* kbase = Ks + l32 * ROW;
+      int koff[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) koff[i] = k_slot(l32, 2 * i + g) << 4;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         u32x4_t kop[KS];
-        const int kr = kb * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          kop[ks] = *reinterpret_cast<const u32x4_t*>(Ks + kr * ROW + (k_slot(kr, ks * 2 + g) << 4));
+          kop[ks] = *reinterpret_cast<const u32x4_t*>(kbase + kb * 32 * ROW + (ks >> 2) * 128 +
+                                                      koff[ks & 3]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
@@ -250,18 +257,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         // steps).  V^T operands come from transpose reads; those of the next
         // (block, step) are read while the current MFMAs run.
         const int r16 = lane & 15;
-        const int colq = ((lane >> 4) & 1) * 16 + (r16 & 3) * 4;  // first of 4 columns
+        // keys of this lane half: {4g..4g+3} and {8+4g..8+4g+3} of each 16-key
+        // step: rows 16 step + 4 g + r16 / 4 (+ 8); columns 32 mb + 16 (lane / 16
+        // & 1) + 4 (r16 & 3).  The swizzle sees only the row's low two bits and
+        // chunk bits 1..2, so two per-lane offsets cover every column block.
+        const int cq = ((lane >> 4) & 1) * 2 + ((r16 & 3) >> 1);  // chunk within 32 columns
+        const unsigned char* vbase = Vs + (g * 4 + (r16 >> 2)) * ROW + (r16 & 1) * 8;
+        int voff[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) voff[i] = v_slot(r16 >> 2, 4 * i + cq) << 4;
         auto read_v = [&](int kb, int half, u32x4_t (&dst)[MB]) {
-          // keys of this lane half: {4g..4g+3} and {8+4g..8+4g+3} of the 16-key step
-          const int ra = kb * 32 + half * 16 + g * 4 + (r16 >> 2);
-          const int rb = ra + 8;
+          const unsigned char* va = vbase + (kb * 32 + half * 16) * ROW;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            const int col = mb * 32 + colq;
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_t*)(Vs + ra * ROW + (v_slot(ra, col >> 3) << 4) + (col & 7) * 2));
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_t*)(Vs + rb * ROW + (v_slot(rb, col >> 3) << 4) + (col & 7) * 2));
+            const int off = (mb >> 1) * 128 + voff[mb & 1];
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + off));
+            const s16x4_t hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 8 * ROW + off));
             const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
             const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
             dst[mb] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
