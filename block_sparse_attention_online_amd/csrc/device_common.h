@@ -69,6 +69,30 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// The lane index, computed afresh at each use (the asm keeps the compiler from
+// merging it with other copies): lets code deep in a loop derive lane-dependent
+// offsets in two instructions instead of holding them in registers all along.
+__device__ __forceinline__ int lane_id_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Lane l combined with lane l ^ 32, without LDS or an address register:
+// v_permlane32_swap with x as both operands returns lanes 0..31 of x in both
+// halves of its first result and lanes 32..63 in both halves of the second.
+// Both lanes of a pair get the same value (same operand order).
+__device__ __forceinline__ float max_xor32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Max over all 64 lanes, returned to every lane: DPP within each row of 16
 // lanes, then the four row results through readlane (no LDS round trips).
 __device__ __forceinline__ float wave_max(float x) {

@@ -10,11 +10,12 @@
 // multiply of skipped blocks.
 //
 // Design (one workgroup = one 128-row query tile of NH query heads that share
-// a KV head -- NH = 2 at D = 64 when the group size is even, else 1 -- 4 waves
-// of 32 rows, one workgroup per compute unit):
+// a KV head -- NH = 2 when the group size is even, else 1 -- with 4 waves of
+// 32 rows per head, one workgroup per compute unit):
 //  * The NH heads visit the same key/value tiles in the same order, so every
 //    tile brought into LDS serves all of them; each head keeps its own
-//    128-row skip decision and its own running state.
+//    128-row skip decision and its own running state.  With NH = 2 every SIMD
+//    runs two waves, so one wave's exponentials overlap the other's MFMAs.
 //  * K and V tiles move from global memory straight into LDS
 //    (global_load_lds, 16 bytes per lane, no registers), into a two-stage
 //    ring: the next tile's loads are in flight while the current tile is
@@ -32,9 +33,9 @@
 //    transpose reads (each 16-lane group turns 4 keys x 16 value columns into
 //    4 keys per column).
 //  * The skip decision: per row delta = tile_max - m (log2 units), the max over
-//    the wave's 32 rows by shuffles, the max over the 4 waves through LDS;
+//    the wave's 32 rows by DPP, the max over the head's 4 waves through LDS;
 //    skip when it is below log2(threshold).  The branch is uniform over the
-//    workgroup, so a skipped tile issues no exp and no P.V MFMA at all.
+//    head's waves, so a skipped tile issues no exp and no P.V MFMA at all.
 
 #include "device_common.h"
 #include "launch.h"
@@ -42,8 +43,7 @@
 namespace ssattn {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kRowWaves = 4;  // waves per head: 4 x 32 rows
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -55,14 +55,16 @@ __device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r & 7); }
 __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r & 3) << 1); }
 
 template <int D, int NH>
-__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int NW = kRowWaves * NH;         // waves in the workgroup
   constexpr int KCH = D / 8;                 // 16-byte chunks per row
   constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
   constexpr int MB = D / 32;                 // 32-wide value-column blocks
   constexpr int ROW = D * 2;                 // bytes per row
   constexpr int TILE_BYTES = kTile * ROW;    // one K or V tile
   constexpr int ROWS_PER_LOAD = 64 / KCH;    // rows one wave instruction covers
-  constexpr int LOADS = kTile / ROWS_PER_LOAD / kWaves;  // per wave per tile (each of K, V)
+  constexpr int LOADS = kTile / ROWS_PER_LOAD / NW;  // per wave per tile (each of K, V)
+  static_assert(LOADS >= 1 && LOADS * ROWS_PER_LOAD * NW == kTile, "tile split");
 
   // Two-stage ring.  Each stage is its own LDS object, and the tile loop is
   // unrolled by two so every access names its stage at compile time: then the
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   __shared__ __attribute__((aligned(1024))) unsigned char vst0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char kst1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char vst1[TILE_BYTES];
-  __shared__ float red[NH][kWaves];
+  __shared__ float red[NH][kRowWaves];
 
   const int nQ = (a.Lq + kTile - 1) / kTile;
   // Logical order: (batch, KV head, query tile, head set within the group), so
@@ -86,16 +88,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   const int qi = (L / sets) % nQ;
   const int hk = (L / (sets * nQ)) % a.Hkv;
   const int b = L / (sets * nQ * a.Hkv);
-  const int h0 = hk * grp_sz + hs * NH;  // first head of the set
   const int qtile = a.causal ? nQ - 1 - qi : qi;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = w / kRowWaves;              // this wave's head within the set
+  const int wr = w % kRowWaves;              // this wave's 32-row block
+  const int head = hk * grp_sz + hs * NH + hh;
   const int l32 = lane & 31;
   const int g = lane >> 5;  // MFMA k-group of this lane
   const int row0 = qtile * kTile;
-  const int rq = row0 + w * 32 + l32;  // the query row this lane owns
+  const int rq = row0 + wr * 32 + l32;  // the query row this lane owns
   const bool row_ok = rq < a.Lq;
   const int shift = a.Lk - a.Lq;
 
@@ -106,67 +110,83 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 
   const VisitPlan plan = make_visit_plan(qtile, a.Lq, a.Lk, a.causal, a.order);
   const int nK = plan.nK;
-  uint8_t* mrows[NH];
-#pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
-    mrows[hh] = a.mask ? a.mask + ((size_t)(b * a.Hq + h0 + hh) * nQ + qtile) * nK : nullptr;
-    if (mrows[hh] && plan.causal) {
-      for (int j = plan.last + 1 + tid; j < nK; j += kThreads) mrows[hh][j] = 2;
-    }
-  }
+  // this head's mask row; its first wave writes it
+  uint8_t* const mrow = a.mask ? a.mask + ((size_t)(b * a.Hq + head) * nQ + qtile) * nK : nullptr;
+  const bool mask_writer = mrow && wr == 0;
+  if (mask_writer && plan.causal)
+    for (int j = plan.last + 1 + lane; j < nK; j += 64) mrow[j] = 2;
 
   // Issue the direct-to-LDS loads of tile j into ring stage st.  Wave w covers
   // rows [w * LOADS * ROWS_PER_LOAD, ...); lane l of load i writes LDS row
   // (base row + l / KCH), physical chunk l % KCH, and fetches the logical
   // chunk that the swizzle puts there.  Rows past Lk read the last key row
   // (their scores are masked to -inf, their P is 0).
+  // Addresses: the tile's first row is a wave-uniform base, the lane's row
+  // within the tile (< 128, clamped to the last key) and chunk a 32-bit offset.
   auto issue_tile = [&](int j, unsigned char* kdst0, unsigned char* vdst0) {
     const int j0 = j * kTile;
-    const int lr = lane / KCH, pc = lane % KCH;
+    const int rlast = a.Lk - 1 - j0;  // last valid row of this tile
+    const unsigned char* kt = reinterpret_cast<const unsigned char*>(kp) + (size_t)j0 * ROW;
+    const unsigned char* vt = reinterpret_cast<const unsigned char*>(vp) + (size_t)j0 * ROW;
+    const int ln = lane_id_fresh();
+    const int lr = ln / KCH, pc = ln % KCH;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int r = (w * LOADS + i) * ROWS_PER_LOAD + lr;
-      const int key = min(j0 + r, a.Lk - 1);
-      const int kc = pc ^ (r & 7);         // inverse of k_slot (an involution)
-      const int vc = pc ^ ((r & 3) << 1);  // inverse of v_slot
+      const unsigned ro = (unsigned)min(r, rlast) * ROW;
+      const unsigned kc = pc ^ (r & 7);         // inverse of k_slot (an involution)
+      const unsigned vc = pc ^ ((r & 3) << 1);  // inverse of v_slot
       const int off = (w * LOADS + i) * ROWS_PER_LOAD * ROW;
       __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(kp + (size_t)key * D + kc * 8),
+          (const void __attribute__((address_space(1)))*)(kt + (ro + (kc << 4))),
           (void __attribute__((address_space(3)))*)(kdst0 + off), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(vp + (size_t)key * D + vc * 8),
+          (const void __attribute__((address_space(1)))*)(vt + (ro + (vc << 4))),
           (void __attribute__((address_space(3)))*)(vdst0 + off), 16, 0, 0);
     }
   };
 
   // Q^T operands: lane holds row rq, head dims [16 ks + 8 g, +8) for every k-step
-  bf16x8_t qf[NH][KS];
-#pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
+  bf16x8_t qf[KS];
+  {
     const unsigned short* qp =
-        static_cast<const unsigned short*>(a.q) + ((size_t)(b * a.Hq + h0 + hh) * a.Lq) * D;
+        static_cast<const unsigned short*>(a.q) + ((size_t)(b * a.Hq + head) * a.Lq) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t u = {0u, 0u, 0u, 0u};
       if (row_ok) u = *reinterpret_cast<const u32x4_t*>(qp + (size_t)rq * D + ks * 16 + g * 8);
-      qf[hh][ks] = as_bf16x8(u);
+      qf[ks] = as_bf16x8(u);
     }
   }
 
-  f32x16_t oacc[NH][MB];
+  f32x16_t oacc[MB];
 #pragma unroll
-  for (int hh = 0; hh < NH; ++hh)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[hh][mb][i] = 0.f;
+    for (int i = 0; i < 16; ++i) oacc[mb][i] = 0.f;
 
   const float c = a.scale * kLog2e;  // raw score -> log2 units
-  float m2[NH], lpart[NH];          // per head: running max (log2 units), this lane's
-#pragma unroll                      // half of the row's denominator
-  for (int hh = 0; hh < NH; ++hh) {
-    m2[hh] = neg_inf();
-    lpart[hh] = 0.f;
+  float m2 = neg_inf();              // running max of row rq (log2 units)
+  float lpart = 0.f;                 // this lane's half of the row's denominator
+
+  // per-lane LDS offsets (the parts of the addresses that depend on the swizzle)
+  // K: row kb * 32 + l32, logical chunk 2 ks + g.  The swizzle sees only
+  // l32 & 7 and chunk bits 0..2, so four offsets cover every k-step (bit 3 of
+  // the chunk and the row block are immediate offsets).
+  int koff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) koff[i] = (k_slot(l32, 2 * i + g) << 4) + l32 * ROW;
+  // V^T: keys {4g..4g+3} and {8+4g..8+4g+3} of each 16-key step, rows
+  // 16 step + 4 g + r16 / 4 (+ 8); columns 32 mb + 16 (lane / 16 & 1) +
+  // 4 (r16 & 3).  The swizzle sees only the row's low two bits and chunk bits
+  // 1..2, so two offsets cover every column block.
+  const int r16 = lane & 15;
+  int voff[2];
+  {
+    const int cq = ((lane >> 4) & 1) * 2 + ((r16 & 3) >> 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      voff[i] = (v_slot(r16 >> 2, 4 * i + cq) << 4) + (g * 4 + (r16 >> 2)) * ROW + (r16 & 1) * 8;
   }
 
   if (plan.count > 0) issue_tile(plan.tile_at(0), kst0, vst0);
@@ -182,143 +202,124 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     // the stage of tile t-1 is free: start tile t+1
     if (t + 1 < plan.count) issue_tile(plan.tile_at(t + 1), Kn, Vn);
 
+    // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 rows
+    f32x16_t sacc[4];
 #pragma unroll
-    for (int hh = 0; hh < NH; ++hh) {
-      // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 rows (K operands read from
-      // LDS just before each block's MFMAs)
-      f32x16_t sacc[4];
-      // row kb * 32 + l32, logical chunk 2 ks + g: the swizzle sees only
-      // l32 & 7 and chunk bits 0..2, so four per-lane offsets cover every k-step
-      // (bit 3 of the chunk and the row block are immediate offsets)
-      const unsigned char* kbase = Ks + l32 * ROW;
-      int koff[4];
+    for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) koff[i] = k_slot(l32, 2 * i + g) << 4;
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      // K operands four k-steps at a time (register budget of two waves per SIMD)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        u32x4_t kop[KS];
+      for (int k4 = 0; k4 < KS; k4 += 4) {
+        u32x4_t kop[4];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kop[ks] = *reinterpret_cast<const u32x4_t*>(kbase + kb * 32 * ROW + (ks >> 2) * 128 +
-                                                      koff[ks & 3]);
+        for (int ks = 0; ks < 4; ++ks)
+          kop[ks] = *reinterpret_cast<const u32x4_t*>(Ks + kb * 32 * ROW + (k4 >> 2) * 128 +
+                                                      koff[ks]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), qf[hh][ks],
+        for (int ks = 0; ks < 4; ++ks)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), qf[k4 + ks],
                                                             sacc[kb], 0, 0, 0);
       }
+    }
 
-      // ---- mask: keys past Lk, and causal keys past row + shift
-      const bool need_mask = (j0 + kTile > a.Lk) || (a.causal && j0 + kTile - 1 > row0 + shift);
-      if (need_mask) {
-        const int lim = a.causal ? min(a.Lk - 1, rq + shift) : a.Lk - 1;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = j0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-            if (key > lim) sacc[kb][i] = neg_inf();
-          }
-      }
-
-      // ---- tile max of the row (raw units), both lane halves
-      float tmax = neg_inf();
+    // ---- mask: keys past Lk, and causal keys past row + shift
+    const bool need_mask = (j0 + kTile > a.Lk) || (a.causal && j0 + kTile - 1 > row0 + shift);
+    if (need_mask) {
+      const int lim = a.causal ? min(a.Lk - 1, rq + shift) : a.Lk - 1;
+      const int kg = j0 + (lane_id_fresh() >> 5) * 4;  // this lane half's first key
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-      const float tmax2 = tmax * c;
-
-      float delta = neg_inf();
-      if (row_ok && tmax2 != neg_inf()) delta = (m2[hh] == neg_inf()) ? pos_inf() : tmax2 - m2[hh];
-      delta = wave_max(delta);
-      if (lane == 0) red[hh][w] = delta;
-      __syncthreads();  // red[] visible
-      const float dblk = fmaxf(fmaxf(red[hh][0], red[hh][1]), fmaxf(red[hh][2], red[hh][3]));
-      const bool skip = dblk < a.log2_thr;
-      if (mrows[hh] && tid == 0) mrows[hh][j] = skip ? 1 : 0;
-
-      const float m2n = fmaxf(m2[hh], tmax2);
-      if (!skip) {
-        const float mref = (m2n == neg_inf()) ? 0.f : m2n;
-        // rescale only when some row's running max grew (the factor is
-        // exactly 1 for every other row)
-        if (__builtin_amdgcn_ballot_w64(m2n != m2[hh]) != 0) {
-          const float alpha = fast_exp2(m2[hh] - mref);
-          lpart[hh] *= alpha;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[hh][mb][i] *= alpha;
+        for (int i = 0; i < 16; ++i) {
+          const int key = kg + kb * 32 + (i >> 2) * 8 + (i & 3);
+          if (key > lim) sacc[kb][i] = neg_inf();
         }
-        // ---- per 32-key block: exponentials, then O^T += V^T P^T (two 16-key
-        // steps).  V^T operands come from transpose reads; those of the next
-        // (block, step) are read while the current MFMAs run.
-        const int r16 = lane & 15;
-        // keys of this lane half: {4g..4g+3} and {8+4g..8+4g+3} of each 16-key
-        // step: rows 16 step + 4 g + r16 / 4 (+ 8); columns 32 mb + 16 (lane / 16
-        // & 1) + 4 (r16 & 3).  The swizzle sees only the row's low two bits and
-        // chunk bits 1..2, so two per-lane offsets cover every column block.
-        const int cq = ((lane >> 4) & 1) * 2 + ((r16 & 3) >> 1);  // chunk within 32 columns
-        const unsigned char* vbase = Vs + (g * 4 + (r16 >> 2)) * ROW + (r16 & 1) * 8;
-        int voff[2];
+    }
+
+    // ---- tile max of the row (raw units), both lane halves
+    float tmax = neg_inf();
 #pragma unroll
-        for (int i = 0; i < 2; ++i) voff[i] = v_slot(r16 >> 2, 4 * i + cq) << 4;
-        auto read_v = [&](int kb, int half, u32x4_t (&dst)[MB]) {
-          const unsigned char* va = vbase + (kb * 32 + half * 16) * ROW;
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const int off = (mb >> 1) * 128 + voff[mb & 1];
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + off));
-            const s16x4_t hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 8 * ROW + off));
-            const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
-            const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
-            dst[mb] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
-          }
-        };
-        u32x4_t vop[2][MB];
-        read_v(0, 0, vop[0]);
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
+    tmax = max_xor32(tmax);
+    const float tmax2 = tmax * c;
+
+    float delta = neg_inf();
+    if (row_ok && tmax2 != neg_inf()) delta = (m2 == neg_inf()) ? pos_inf() : tmax2 - m2;
+    delta = wave_max(delta);
+    if (lane == 0) red[hh][wr] = delta;
+    __syncthreads();  // red[] visible
+    float dblk = red[hh][0];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          bf16x8_t pb[2];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            unsigned int pw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p0 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e], c, -mref));
-              const float p1 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e + 1], c, -mref));
-              lpart[hh] += p0 + p1;
-              pw[e] = pack_bf16x2(p0, p1);
-            }
-            u32x4_t pu = {pw[0], pw[1], pw[2], pw[3]};
-            pb[half] = as_bf16x8(pu);
-          }
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int st = kb * 2 + half;
-            if (st + 1 < 8) read_v((st + 1) >> 1, (st + 1) & 1, vop[(st + 1) & 1]);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              oacc[hh][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[st & 1][mb]),
-                                                                    pb[half], oacc[hh][mb], 0, 0, 0);
-          }
-        }
-      } else if (a.thr_above_1 && m2n > m2[hh]) {
-        const float alpha = fast_exp2(m2[hh] - m2n);
-        lpart[hh] *= alpha;
+    for (int i = 1; i < kRowWaves; ++i) dblk = fmaxf(dblk, red[hh][i]);
+    const bool skip = dblk < a.log2_thr;
+    if (mask_writer && lane == 0) mrow[j] = skip ? 1 : 0;
+
+    const float m2n = fmaxf(m2, tmax2);
+    if (!skip) {
+      const float mref = (m2n == neg_inf()) ? 0.f : m2n;
+      // rescale only when some row's running max grew (the factor is exactly
+      // 1 for every other row)
+      if (__builtin_amdgcn_ballot_w64(m2n != m2) != 0) {
+        const float alpha = fast_exp2(m2 - mref);
+        lpart *= alpha;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[hh][mb][i] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
       }
-      m2[hh] = m2n;
-      // keep the heads' live ranges apart: one set of score accumulators
-      __builtin_amdgcn_sched_barrier(0);
+      // ---- per 32-key block: exponentials, then O^T += V^T P^T (two 16-key
+      // steps, V^T operands from transpose reads).
+      auto read_v = [&](int kb, int half, u32x4_t (&dst)[MB]) {
+        const unsigned char* va = Vs + (kb * 32 + half * 16) * ROW;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int off = (mb >> 1) * 128 + voff[mb & 1];
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + off));
+          const s16x4_t hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 8 * ROW + off));
+          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+          const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+          dst[mb] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+        }
+      };
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          unsigned int pw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e], c, -mref));
+            const float p1 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e + 1], c, -mref));
+            lpart += p0 + p1;
+            pw[e] = pack_bf16x2(p0, p1);
+          }
+          u32x4_t pu = {pw[0], pw[1], pw[2], pw[3]};
+          pb[half] = as_bf16x8(pu);
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4_t vop[MB];
+          read_v(kb, half, vop);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[mb]), pb[half],
+                                                              oacc[mb], 0, 0, 0);
+        }
+      }
+    } else if (a.thr_above_1 && m2n > m2) {
+      const float alpha = fast_exp2(m2 - m2n);
+      lpart *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
     }
+    m2 = m2n;
   };
 
   for (int t = 0; t < plan.count; t += 2) {
@@ -327,23 +328,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   }
 
   // ---- epilogue: O / l, lane holds columns 32 mb + 8 (i/4) + 4 g + i%4 of row rq
+  const float l = sum_xor32(lpart);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  unsigned short* op = static_cast<unsigned short*>(a.out) + ((size_t)(b * a.Hq + head) * a.Lq) * D;
+  if (row_ok) {
 #pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
-    const float l = lpart[hh] + shfl_xor_f(lpart[hh], 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    unsigned short* op =
-        static_cast<unsigned short*>(a.out) + ((size_t)(b * a.Hq + h0 + hh) * a.Lq) * D;
-    if (row_ok) {
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int col = mb * 32 + i4 * 8 + g * 4;
-          u32x2_t pk = {pack_bf16x2(oacc[hh][mb][i4 * 4 + 0] * inv, oacc[hh][mb][i4 * 4 + 1] * inv),
-                        pack_bf16x2(oacc[hh][mb][i4 * 4 + 2] * inv, oacc[hh][mb][i4 * 4 + 3] * inv)};
-          *reinterpret_cast<u32x2_t*>(op + (size_t)rq * D + col) = pk;
-        }
-    }
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int col = mb * 32 + i4 * 8 + g * 4;
+        u32x2_t pk = {pack_bf16x2(oacc[mb][i4 * 4 + 0] * inv, oacc[mb][i4 * 4 + 1] * inv),
+                      pack_bf16x2(oacc[mb][i4 * 4 + 2] * inv, oacc[mb][i4 * 4 + 3] * inv)};
+        *reinterpret_cast<u32x2_t*>(op + (size_t)rq * D + col) = pk;
+      }
   }
 }
 
@@ -353,17 +350,18 @@ bool prefill_bf16_supported(int D, int Dv) { return D == Dv && (D == 64 || D == 
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const int nQ = (a.Lq + kTile - 1) / kTile;
-  // heads per workgroup: two at D = 64 when the group size is even; at D = 128
-  // two heads' accumulators and Q operands no longer fit the register file
-  const int nh = (a.D == 64 && (a.Hq / a.Hkv) % 2 == 0) ? 2 : 1;
+  const int nh = ((a.Hq / a.Hkv) % 2 == 0) ? 2 : 1;  // heads per workgroup
   const dim3 grid((unsigned)((size_t)nQ * (a.Hq / nh) * a.B));
   if (a.D == 64) {
     if (nh == 2)
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, 2>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, 2>), grid, dim3(64 * kRowWaves * 2), 0, s, a);
     else
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, 1>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, 1>), grid, dim3(64 * kRowWaves), 0, s, a);
   } else {
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, 1>), grid, dim3(kThreads), 0, s, a);
+    if (nh == 2)
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 2>), grid, dim3(64 * kRowWaves * 2), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 1>), grid, dim3(64 * kRowWaves), 0, s, a);
   }
   return hipGetLastError();
 }
