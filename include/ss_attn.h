@@ -153,7 +153,7 @@ typedef enum { SS_SPLIT_CHAINED = 0, SS_SPLIT_INDEPENDENT = 1 } ss_split_mode;
  * ss_attn_decode_workspace_bytes() bytes; its contents on entry do not
  * matter, and two calls that overlap in time must not share one.  Supported:
  * (D, Dv) = (64, 64) or (128, 128) with Hq/Hkv in {1, 2, 4, 8}; (576, 512)
- * with v == NULL and Hq/Hkv a multiple of 16 up to 128.
+ * with v == NULL and Hq/Hkv in {64, 128}.
  *
  * ss_attn_decode is ss_attn_decode_ex with split_mode CHAINED.
  */
