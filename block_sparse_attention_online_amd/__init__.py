@@ -63,6 +63,19 @@ class _DecodeParams(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+class _DecodePagedParams(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+                ("v_cache", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("thresholds", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("B", ctypes.c_int), ("Hq", ctypes.c_int),
+                ("Hkv", ctypes.c_int), ("D", ctypes.c_int), ("Dv", ctypes.c_int),
+                ("block_size", ctypes.c_int), ("max_blocks_per_seq", ctypes.c_int),
+                ("num_blocks", ctypes.c_int), ("max_seq_len", ctypes.c_int),
+                ("scale", ctypes.c_float), ("factor", ctypes.c_float),
+                ("num_splits", ctypes.c_int), ("skip_mask_out", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 SPLIT_MODES = {"chained": 0, "independent": 1}
 
 _LIB = None
@@ -75,6 +88,7 @@ _SIGNATURES = {
     "ss_attn_prefill_ex": (_I, [ctypes.POINTER(_PrefillParams), _P]),
     "ss_attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _P, _SZ, _P]),
     "ss_attn_decode_ex": (_I, [ctypes.POINTER(_DecodeParams), _P]),
+    "ss_attn_decode_paged": (_I, [ctypes.POINTER(_DecodePagedParams), _P]),
     "ss_attn_decode_partial": (_I, [ctypes.POINTER(_DecodeParams), _P]),
     "ss_attn_decode_combine": (_I, [ctypes.POINTER(_DecodeParams), _P]),
     "ss_attn_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
@@ -284,6 +298,50 @@ def ss_attn_decode_ex(q, k, v=None, out=None, *, dv=None, scale=None, threshold=
     p, _, _ = _decode_params(q, k, v, out, dv, scale, threshold, num_splits, split_mode,
                              skip_mask, workspace)
     _check(lib().ss_attn_decode_ex(ctypes.byref(p), _stream(stream, q.device)))
+    return out
+
+
+def ss_attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len,
+                         out=None, scale=None, factor=0.0, thresholds=None, num_splits=0,
+                         skip_mask=None, workspace=None, stream=None):
+    """Skip-softmax decode over a block-paged cache with per-sequence lengths.
+
+    q [B,Hq,D] bf16; k_cache/v_cache [num_blocks,Hkv,block_size,D] bf16;
+    block_table int32 [B,max_blocks]; seq_lens int32 [B] (all GPU tensors).
+    Sequence b uses ``thresholds[b]`` (fp32 GPU tensor) when given, else
+    ``factor / seq_lens[b]``.  Returns ``out`` [B,Hq,D]; fills ``skip_mask``
+    (u8 [B,Hkv,ceil(max_seq_len/128)], 2 past a sequence's end) when given."""
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and the caches [num_blocks, Hkv, block_size, D]")
+    B, Hq, D = q.shape
+    nblk, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape[:3]) != (nblk, Hkv, bs):
+        raise ValueError(f"cache shapes k{tuple(k_cache.shape)} v{tuple(v_cache.shape)} vs q{tuple(q.shape)}")
+    Dv = v_cache.shape[3]
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    dt = torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=dt, device=q.device)
+    mptr = None
+    if skip_mask is not None:
+        if tuple(skip_mask.shape) != mask_shape_decode(B, Hkv, max_seq_len):
+            raise ValueError(f"skip_mask must be {mask_shape_decode(B, Hkv, max_seq_len)}")
+        mptr = _dev(skip_mask, "skip_mask", torch.uint8)
+    if workspace is None:
+        need = ss_attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, D, Dv, num_splits)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    tptr = None if thresholds is None else _dev(thresholds, "thresholds", torch.float32)
+    p = _DecodePagedParams(_dev(q, "q", dt), _dev(k_cache, "k_cache", dt),
+                           _dev(v_cache, "v_cache", dt), _dev(block_table, "block_table", torch.int32),
+                           _dev(seq_lens, "seq_lens", torch.int32), tptr, _dev(out, "out", dt),
+                           B, Hq, Hkv, D, Dv, bs, block_table.shape[1], nblk, int(max_seq_len),
+                           float(scale), float(factor), int(num_splits), mptr,
+                           _dev(workspace, "workspace"),
+                           workspace.numel() * workspace.element_size())
+    _check(lib().ss_attn_decode_paged(ctypes.byref(p), _stream(stream, q.device)))
     return out
 
 

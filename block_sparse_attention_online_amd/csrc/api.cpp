@@ -365,7 +365,7 @@ int prepare_decode(const ss_decode_params* p, bool stage_partial, ssattn::Decode
 extern "C" {
 
 int ss_attn_decode_partial(const ss_decode_params* p, hipStream_t stream) {
-  ssattn::DecodeArgs a;
+  ssattn::DecodeArgs a{};
   DecodeKernel k;
   if (int rc = prepare_decode(p, true, &a, &k)) return rc;
   a.lb_tag = next_tag();
@@ -376,11 +376,86 @@ int ss_attn_decode_partial(const ss_decode_params* p, hipStream_t stream) {
 }
 
 int ss_attn_decode_combine(const ss_decode_params* p, hipStream_t stream) {
-  ssattn::DecodeArgs a;
+  ssattn::DecodeArgs a{};
   DecodeKernel k;
   if (int rc = prepare_decode(p, false, &a, &k)) return rc;
   if (!p->out) return fail(SS_ERR_INVALID_ARG, "out must be non-null");
   hipError_t e = ssattn::launch_decode_combine(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
+int ss_attn_decode_paged(const ss_decode_paged_params* p, hipStream_t stream) {
+  if (!p) return fail(SS_ERR_INVALID_ARG, "params is null");
+  if (!p->q || !p->k_cache || !p->v_cache || !p->block_table || !p->seq_lens || !p->out)
+    return fail(SS_ERR_INVALID_ARG,
+                "q, k_cache, v_cache, block_table, seq_lens and out must be non-null");
+  if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->D <= 0 || p->Dv <= 0 ||
+      p->max_blocks_per_seq <= 0 || p->num_blocks <= 0 || p->max_seq_len <= 0)
+    return fail(SS_ERR_INVALID_ARG, "sizes must be positive");
+  if (p->max_seq_len > kMaxLen)
+    return fail(SS_ERR_INVALID_ARG, "max_seq_len above %d is not supported", kMaxLen);
+  if (p->Hq % p->Hkv)
+    return fail(SS_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  int block_log2 = -1;
+  for (int l = 4; l <= 7; ++l)
+    if (p->block_size == (1 << l)) block_log2 = l;
+  if (block_log2 < 0)
+    return fail(SS_ERR_INVALID_ARG, "block_size must be 16, 32, 64 or 128 (got %d)",
+                p->block_size);
+  if ((int64_t)p->max_blocks_per_seq * p->block_size < p->max_seq_len)
+    return fail(SS_ERR_INVALID_ARG, "max_seq_len %d exceeds %d blocks of %d keys",
+                p->max_seq_len, p->max_blocks_per_seq, p->block_size);
+  if (p->num_splits < 0) return fail(SS_ERR_INVALID_ARG, "num_splits must be >= 0");
+  if (int rc = check_scale(p->scale)) return rc;
+  if (!(p->factor >= 0.f) || !std::isfinite(p->factor))
+    return fail(SS_ERR_INVALID_ARG, "factor must be finite and >= 0 (got %g)", (double)p->factor);
+  const int group = p->Hq / p->Hkv;
+  if (decode_kernel(p->D, p->Dv, group, false) != DecodeKernel::kGqa)
+    return fail(SS_ERR_UNSUPPORTED, "paged decode supports D == Dv in {64, 128} and Hq/Hkv in "
+                "{1, 2, 4, 8} (got D=%d Dv=%d group=%d)", p->D, p->Dv, group);
+  const DecodePlan pl =
+      plan_decode(p->B, p->Hq, p->Hkv, p->max_seq_len, p->D, p->Dv, false, p->num_splits, true);
+  if (!p->workspace || p->workspace_bytes < pl.bytes)
+    return fail(SS_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", pl.bytes,
+                p->workspace_bytes, p->workspace ? "" : ", null");
+  char* ws = static_cast<char*>(p->workspace);
+  ssattn::DecodeArgs a{};
+  a.q = p->q;
+  a.k = p->k_cache;
+  a.v = p->v_cache;
+  a.out = p->out;
+  a.mask = p->skip_mask_out;
+  a.part_o = reinterpret_cast<float*>(ws + pl.o_off);
+  a.part_lse = reinterpret_cast<float*>(ws + pl.lse_off);
+  a.lb_slot = reinterpret_cast<unsigned long long*>(ws + pl.slot_off);
+  a.lb_xchg = nullptr;
+  a.lb_timeouts = reinterpret_cast<unsigned int*>(ws + pl.timeout_off);
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.Lk = p->max_seq_len;
+  a.D = p->D;
+  a.Dv = p->Dv;
+  a.num_splits = pl.subs;
+  a.tiles_per_split = pl.tiles_per_sub;
+  a.chain_tiles = pl.chain_tiles;
+  a.subs_per_chain = pl.subs_per_chain;
+  a.scale = p->scale;
+  a.log2_thr = 0.f;  // per sequence on the device
+  a.thr_above_1 = 0;
+  a.lb_tag = next_tag();
+  a.block_table = p->block_table;
+  a.seq_lens = p->seq_lens;
+  a.thresholds = p->thresholds;
+  a.factor = p->factor;
+  a.block_log2 = block_log2;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.num_blocks = p->num_blocks;
+  a.mask_tiles = (int)ceil_div(p->max_seq_len, SS_TILE_KEYS);
+  hipError_t e = ssattn::launch_decode_gqa_paged(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "paged decode launch");
+  e = ssattn::launch_decode_combine(a, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
 }

@@ -51,8 +51,8 @@ constexpr int max_tiles() { return 64 / G; }  // score LDS: 128 keys x G x 4 B x
 
 typedef __attribute__((ext_vector_type(4))) float f4_t;
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(DecodeArgs a) {
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int TMAX = max_tiles<G>();
   constexpr int KS = D / 32;          // MFMA k-steps over the head dimension
   constexpr int KL = 2 * KS;          // 16-byte K loads per lane per tile
@@ -69,13 +69,23 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(Dec
   __shared__ float s_lred[kWaves][G];
   __shared__ int s_surv[TMAX];
   __shared__ int s_nsurv;
+  __shared__ int s_blk[PAGED ? TMAX * kTile / 16 : 1];  // paged: this sub-split's cache blocks
 
   const int S = a.num_splits;  // sub-splits per (batch, KV head)
   const int sub = blockIdx.x % S;
   const int pair = blockIdx.x / S;  // b * Hkv + hk
   const int hk = pair % a.Hkv;
   const int b = pair / a.Hkv;
-  const int nK = (a.Lk + kTile - 1) / kTile;
+  // the sequence's length and threshold (paged: per sequence)
+  int Lk = a.Lk;
+  float log2_thr = a.log2_thr;
+  if constexpr (PAGED) {
+    Lk = min(max(a.seq_lens[b], 0), a.Lk);
+    const float thr = a.thresholds ? a.thresholds[b]
+                                   : (Lk > 0 ? (float)((double)a.factor / (double)Lk) : 0.f);
+    log2_thr = thr > 0.f ? (float)log2((double)thr) : neg_inf();
+  }
+  const int nK = (Lk + kTile - 1) / kTile;
   const int chain = sub / a.subs_per_chain;
   const int link = sub % a.subs_per_chain;
   const int chain_t0 = chain * a.chain_tiles;
@@ -89,6 +99,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(Dec
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
+  if constexpr (PAGED) {
+    // tiles of this sub-split's range past the sequence's end: not visited
+    const int mask_tiles = a.mask_tiles;
+    const int t_end = min(min(t0 + a.tiles_per_split, chain_t0 + a.chain_tiles), mask_tiles);
+    if (a.mask)
+      for (int t = max(t0, t0 + T) + threadIdx.x; t < t_end; t += kThreads)
+        a.mask[(size_t)pair * mask_tiles + t] = 2;
+  }
   if (T == 0) {  // an empty trailing link: nothing to publish, nobody waits on it
     for (int idx = tid; idx < G * D; idx += kThreads) {
       const size_t rowid = ((size_t)sub * a.B + b) * a.Hq + hk * G + idx / D;
@@ -101,9 +119,29 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(Dec
   const unsigned short* qp =
       static_cast<const unsigned short*>(a.q) + ((size_t)b * a.Hq + hk * G) * D;
   const unsigned short* kp =
-      static_cast<const unsigned short*>(a.k) + ((size_t)pair * a.Lk) * D;
+      static_cast<const unsigned short*>(a.k) + (PAGED ? 0 : ((size_t)pair * a.Lk) * D);
   const unsigned short* vp =
-      static_cast<const unsigned short*>(a.v) + ((size_t)pair * a.Lk) * D;
+      static_cast<const unsigned short*>(a.v) + (PAGED ? 0 : ((size_t)pair * a.Lk) * D);
+  // paged: the cache blocks of keys [t0 * 128, min((t0 + T) * 128, Lk)), block
+  // ids clamped into the cache
+  const int blk0 = PAGED ? (t0 * kTile) >> a.block_log2 : 0;
+  if constexpr (PAGED) {
+    const int nb = ((min((t0 + T) * kTile, Lk) - 1) >> a.block_log2) - blk0 + 1;
+    for (int i = tid; i < nb; i += kThreads)
+      s_blk[i] = min(max(a.block_table[(size_t)b * a.max_blocks + blk0 + i], 0), a.num_blocks - 1);
+    __syncthreads();
+  }
+  // first element of key row `key` (Lk > key >= t0 * 128) of K, or of V
+  auto row = [&](const unsigned short* base, int key) -> const unsigned short* {
+    if constexpr (PAGED) {
+      const int blk = s_blk[(key >> a.block_log2) - blk0];
+      const size_t r = (((size_t)blk * a.Hkv + hk) << a.block_log2) +
+                       (key & ((1 << a.block_log2) - 1));
+      return base + r * D;
+    } else {
+      return base + (size_t)key * D;
+    }
+  };
   const float c = a.scale * kLog2e;
 
   // ---------------------------------------------------------------- 1. K pass
@@ -126,8 +164,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(Dec
       const int j0 = (t0 + tl) * kTile + w * kKeysPerWave;
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
-        const int key = min(j0 + i * RPI + lrow, a.Lk - 1);
-        dst[i] = *reinterpret_cast<const u32x4_t*>(kp + (size_t)key * D + lch * 8);
+        const int key = min(j0 + i * RPI + lrow, Lk - 1);
+        dst[i] = *reinterpret_cast<const u32x4_t*>(row(kp, key) + lch * 8);
       }
     };
     unsigned char* stage = kstage[w];
@@ -162,7 +200,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(Dec
         for (int i = 0; i < 4; ++i) {
           const int kin = blk * 16 + grp * 4 + i;  // key within the wave's 32
           float s = acc[blk][i] * c;
-          if (jw + kin >= a.Lk) s = neg_inf();
+          if (jw + kin >= Lk) s = neg_inf();
           if (l16 < G) sc[(tl * kTile + w * kKeysPerWave + kin) * G + l16] = s;
           pm = fmaxf(pm, s);
         }
@@ -258,13 +296,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(Dec
       if (tm[r] != neg_inf()) dr = (M == neg_inf()) ? pos_inf() : tm[r] - M;
       dmax = fmaxf(dmax, dr);
     }
-    const bool skip = dmax < a.log2_thr;
+    const bool skip = dmax < log2_thr;
     const bool kept = valid && !skip;
     const unsigned long long bits = __ballot(kept);
     const int idx = __popcll(bits & ((1ull << lane) - 1ull));
     if (kept) s_surv[idx] = lane;
     if (lane == 0) s_nsurv = __popcll(bits);
-    if (valid && a.mask) a.mask[(size_t)pair * nK + t0 + lane] = skip ? 1 : 0;
+    if (valid && a.mask)
+      a.mask[(size_t)pair * (PAGED ? a.mask_tiles : nK) + t0 + lane] = skip ? 1 : 0;
 #pragma unroll
     for (int r = 0; r < G; ++r)
       if (lane == r) s_mref[r] = cmax[r];
@@ -289,8 +328,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(Dec
       const int j0 = (t0 + s_surv[si]) * kTile + w * kKeysPerWave;
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
-        const int key = min(j0 + it * KPI + kq, a.Lk - 1);
-        dst[it] = *reinterpret_cast<const u32x4_t*>(vp + (size_t)key * D + cc * 8);
+        const int key = min(j0 + it * KPI + kq, Lk - 1);
+        dst[it] = *reinterpret_cast<const u32x4_t*>(row(vp, key) + cc * 8);
       }
     };
     auto accum_v = [&](int si, const u32x4_t (&src)[IT]) {
@@ -366,14 +405,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void decode_gqa_kernel(Dec
   }
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s, int G) {
   const dim3 grid((unsigned)((size_t)a.num_splits * a.Hkv * a.B));
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_gqa_kernel<D, 1>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_gqa_kernel<D, 2>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_gqa_kernel<D, 4>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_gqa_kernel<D, 8>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_gqa_kernel<D, 1, PAGED>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_gqa_kernel<D, 2, PAGED>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_gqa_kernel<D, 4, PAGED>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_gqa_kernel<D, 8, PAGED>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -390,7 +429,12 @@ int decode_gqa_max_tiles(int group) { return 64 / group; }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  return a.D == 64 ? launch_d<64>(a, s, G) : launch_d<128>(a, s, G);
+  return a.D == 64 ? launch_d<64, false>(a, s, G) : launch_d<128, false>(a, s, G);
+}
+
+hipError_t launch_decode_gqa_paged(const DecodeArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  return a.D == 64 ? launch_d<64, true>(a, s, G) : launch_d<128, true>(a, s, G);
 }
 
 }  // namespace ssattn

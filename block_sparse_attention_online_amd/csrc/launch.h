@@ -48,6 +48,19 @@ struct DecodeArgs {
   unsigned long long* lb_xchg;     // latent decode: [S][B][Hkv][2][64] per-tile statistic
                                    // of each half of the head group (null otherwise)
   unsigned int* lb_timeouts;       // count of look-back waits that gave up
+  // Paged caches (GQA decode): k, v point at [num_blocks, Hkv, 2^block_log2, D]
+  // caches, sequence b has seq_lens[b] keys (Lk is their upper bound) whose
+  // blocks are block_table[b][...] ([B][max_blocks]), and its threshold is
+  // thresholds[b], or factor / seq_lens[b] when thresholds is null.  The mask
+  // has mask_tiles entries per (batch, KV head).
+  const int* block_table;
+  const int* seq_lens;
+  const float* thresholds;
+  float factor;
+  int block_log2;
+  int max_blocks;
+  int num_blocks;
+  int mask_tiles;
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
@@ -56,6 +69,7 @@ bool prefill_bf16_supported(int D, int Dv);
 bool prefill_f32_supported(int D, int Dv);
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_gqa_paged(const DecodeArgs& a, hipStream_t s);
 bool decode_gqa_supported(int D, int Dv, int group, bool latent);
 int decode_gqa_max_tiles(int group);  // tiles a split may hold in chained mode
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);

@@ -190,6 +190,56 @@ int ss_attn_decode_ex(const ss_decode_params* p, hipStream_t stream);
 int ss_attn_decode_partial(const ss_decode_params* p, hipStream_t stream);
 int ss_attn_decode_combine(const ss_decode_params* p, hipStream_t stream);
 
+/*
+ * Decode over a block-paged KV cache, one query token per sequence, sequences
+ * of different lengths, each with its own threshold (design page "The
+ * threshold": the threshold is a factor over the sequence length, so every
+ * sequence of a batch gets factor / L_b).  Splits are CHAINED: the decisions
+ * of sequence b are those of one streaming pass over its L_b keys.
+ *
+ *   q            [B, Hq, D] bf16
+ *   k_cache      [num_blocks, Hkv, block_size, D] bf16
+ *   v_cache      [num_blocks, Hkv, block_size, Dv] bf16
+ *   block_table  int32 [B, max_blocks_per_seq]: cache block of each
+ *                block_size-key block of a sequence (device memory)
+ *   seq_lens     int32 [B]: keys of each sequence (device memory)
+ *   thresholds   fp32 [B] (device memory), or NULL: sequence b then uses
+ *                factor / seq_lens[b]; factor 0 is dense
+ *   out          [B, Hq, Dv] bf16 (written)
+ *   skip_mask_out u8 [B, Hkv, ceil(max_seq_len/128)] or NULL (written; 2 marks
+ *                tiles past a sequence's end)
+ *
+ * Host-side checks: shapes as for ss_attn_decode (Dv = D), block_size in
+ * {16, 32, 64, 128}, max_seq_len <= max_blocks_per_seq * block_size, factor
+ * finite and >= 0, workspace of ss_attn_decode_workspace_bytes(B, Hq, Hkv,
+ * max_seq_len, D, Dv, num_splits) bytes.  The device arrays are trusted up to
+ * clamping: a sequence length is clamped into [0, max_seq_len] (0 writes a
+ * zero output row) and a block id into [0, num_blocks).  Thresholds from the
+ * array must be >= 0.
+ */
+typedef struct {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const float* thresholds;
+  void* out;
+  int B, Hq, Hkv, D, Dv;
+  int block_size;
+  int max_blocks_per_seq;
+  int num_blocks;
+  int max_seq_len;
+  float scale;
+  float factor;
+  int num_splits; /* 0 = automatic, as ss_decode_num_splits(..., max_seq_len, ...) */
+  uint8_t* skip_mask_out;
+  void* workspace;
+  size_t workspace_bytes;
+} ss_decode_paged_params;
+
+int ss_attn_decode_paged(const ss_decode_paged_params* p, hipStream_t stream);
+
 /* Bytes of decode workspace for these sizes (num_splits as for
  * ss_attn_decode, 0 = automatic), enough for either split mode.  Returns 0
  * for invalid sizes. */

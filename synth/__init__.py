@@ -7,6 +7,7 @@ inputs from here without sharing any part of the method.
 """
 
 from .generators import (  # noqa: F401
+    paged_decode,
     bf16_round,
     clustered_decode,
     clustered_prefill,

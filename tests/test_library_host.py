@@ -39,6 +39,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["ss_attn_prefill", "ss_attn_prefill_f32", "ss_attn_prefill_ex", "ss_attn_decode",
               "ss_attn_decode_ex", "ss_attn_decode_partial", "ss_attn_decode_combine",
+              "ss_attn_decode_paged",
               "ss_attn_decode_workspace_bytes", "ss_decode_num_splits", "ss_factor",
               "ss_threshold", "ss_gate_enabled", "ss_resolve_threshold", "ss_last_error",
               "ss_version"]:
@@ -239,3 +240,29 @@ def test_binding_refuses_cpu_tensors(ss):
         ss.ss_attn_prefill(q, q, q)
     with pytest.raises(ValueError, match="GPU tensor"):
         ss.ss_attn_decode(q[:, :, 0], q, q)
+
+
+def paged_call(ss, **over):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, thr=None, out=FAKE, B=2, Hq=8, Hkv=2,
+             D=128, Dv=128, bs=16, mb=100, nb=300, L=1600, scale=0.1, factor=10.0, S=0,
+             mask=None, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    p = ss._DecodePagedParams(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["thr"], a["out"],
+                              a["B"], a["Hq"], a["Hkv"], a["D"], a["Dv"], a["bs"], a["mb"],
+                              a["nb"], a["L"], a["scale"], a["factor"], a["S"], a["mask"],
+                              a["ws"], a["wsb"])
+    return ss.lib().ss_attn_decode_paged(ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(bt=None), -1), (dict(sl=None), -1), (dict(B=0), -1), (dict(nb=0), -1),
+    (dict(bs=24), -1), (dict(bs=256), -1), (dict(bs=8), -1),
+    (dict(L=1601), -1),                              # more keys than 100 blocks of 16
+    (dict(factor=-1.0), -1), (dict(factor=float("nan")), -1), (dict(scale=0.0), -1),
+    (dict(Hq=9), -1), (dict(D=96, Dv=96), -2), (dict(Hq=48, Hkv=2), -2),
+    (dict(ws=None), -4), (dict(wsb=64), -4),
+])
+def test_paged_decode_rejects_before_launch(ss, over, code):
+    assert paged_call(ss, **over) == code
+    assert ss.ss_last_error()
+
