@@ -14,6 +14,11 @@
       latent decode (B8, 128 heads, 576-wide latent rows, value = first 512
       columns) at 16K..128K keys: one factor a*exp(0.7 b) fitted so ~70 % of
       tiles skip at every length; K bytes per second and MFMA rate.
+  python -m block_sparse_attention_online_amd.harness paged [--out FILE]
+      paged decode of a serving-like batch (32 sequences of 1K..32K keys,
+      Hq32/Hkv8, D128, 16-key cache blocks): one factor, threshold
+      factor / L_b per sequence, bisected so ~70 % of the batch's tiles skip;
+      skip per length bucket, bytes per second, speedup over threshold 0.
   python -m block_sparse_attention_online_amd.harness decode [--out FILE]
       GQA decode (B16, Hq32/Hkv8, 32768 keys, D128): skip 0.5 / 0.7 / 0.9
       against threshold 0, chained splits.
@@ -370,8 +375,86 @@ def run_decode(args):
     return rows, cols
 
 
+# --------------------------------------------------------------------------- paged decode
+
+def run_paged(args):
+    from synth import paged_decode
+
+    from . import ss_attn_decode_paged
+
+    timer, rows = Timer(), []
+    rng = np.random.default_rng(7000)
+    lens = [int(x) for x in rng.integers(1024, 32769, size=32)]
+    Hq, Hkv, D, bs = 32, 8, 128, 16
+    t = time.time()
+    x = paged_decode(7000, lens, Hq, Hkv, D, D, 64, 3.0, bs)
+    log(f"[paged] generated {sum(lens)} tokens in {time.time() - t:.1f}s")
+    q, kc, vc = x["q"].cuda(), x["k_cache"].cuda(), x["v_cache"].cuda()
+    table, sl = x["block_table"].cuda(), x["seq_lens"].cuda()
+    del x
+    B, L = len(lens), max(lens)
+    ws = torch.empty(ss_attn_decode_workspace_bytes(B, Hq, Hkv, L, D, D, 0), dtype=torch.uint8,
+                     device="cuda")
+    mask = torch.empty(mask_shape_decode(B, Hkv, L), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+
+    def call(factor):
+        ss_attn_decode_paged(q, kc, vc, table, sl, max_seq_len=L, out=out, scale=scale,
+                             factor=factor, skip_mask=mask, workspace=ws)
+
+    def skip_at(factor):
+        call(factor)
+        torch.cuda.synchronize()
+        return skip_fraction(mask)
+
+    nK = [-(-n // 128) for n in lens]
+    kb = sum(lens) * Hkv * D * 2
+    dense_ms = timer.ms(lambda: call(0.0))
+    dense_out = out.clone()
+    emit({"workload": "paged_decode_32seq", "stage": "dense", "tokens": sum(lens),
+          "ms": round(dense_ms, 4), "gbs": round(2 * kb / dense_ms / 1e6, 1)}, rows)
+    # skip is non-decreasing in the factor: bisect it in log space over the batch
+    lo, hi = 1e-3, 1e6
+    if skip_at(hi) < 0.7:
+        factor = hi
+    else:
+        for _ in range(40):
+            mid = math.sqrt(lo * hi)
+            if skip_at(mid) < 0.7:
+                lo = mid
+            else:
+                hi = mid
+        factor = hi
+    ms = timer.ms(lambda: call(factor))
+    s = skip_at(factor)
+    m = mask.cpu().numpy()
+    kept_keys = 0
+    per_bucket = {}
+    for b, n in enumerate(lens):
+        keys = np.full(nK[b], 128)
+        keys[-1] = n - 128 * (nK[b] - 1)
+        mb = m[b, :, :nK[b]]
+        kept_keys += int(((mb == 0) * keys[None, :]).sum())
+        bucket = f"{(n - 1) // 8192 * 8}K-{(n - 1) // 8192 * 8 + 8}K"
+        sk, vis = per_bucket.get(bucket, (0, 0))
+        per_bucket[bucket] = (sk + int((mb == 1).sum()), vis + mb.size)
+    by = kb + kept_keys * D * 2
+    emit({"workload": "paged_decode_32seq", "stage": "sparse", "factor": float(f"{factor:.6g}"),
+          "skip": round(s, 4), "ms": round(ms, 4), "gbs": round(by / ms / 1e6, 1),
+          "frac_hbm": round(by / ms / 1e6 / HBM_PEAK_GBS, 4), "speedup": round(dense_ms / ms, 3),
+          "rel_l2_vs_dense": float(f"{rel_l2_gpu(out, dense_out):.3e}")}, rows)
+    for bucket in sorted(per_bucket, key=lambda k: int(k.split("K")[0])):
+        sk, vis = per_bucket[bucket]
+        emit({"workload": "paged_decode_32seq", "stage": "skip by length", "bucket": bucket,
+              "skip": round(sk / vis, 4)}, rows)
+    cols = ["stage", "tokens", "factor", "bucket", "skip", "ms", "gbs", "frac_hbm", "speedup",
+            "rel_l2_vs_dense"]
+    return rows, cols
+
+
 RUNS = {"prefill": run_prefill_sweep, "video": run_video, "latent": run_latent,
-        "decode": run_decode}
+        "decode": run_decode, "paged": run_paged}
 
 
 def main(argv=None):
