@@ -22,6 +22,12 @@
   python -m block_sparse_attention_online_amd.harness decode [--out FILE]
       GQA decode (B16, Hq32/Hkv8, 32768 keys, D128): skip 0.5 / 0.7 / 0.9
       against threshold 0, chained splits.
+  python -m block_sparse_attention_online_amd.harness stability [--out FILE]
+      GQA decode (Hq32/Hkv8, D128) from 4K to 200K keys, batch sized to ~1 GB
+      of K: a threshold bisected at 32K for 70 % / 90 % skip, then used either
+      unchanged at every length or as a factor (threshold = factor / L); skip
+      and speedup per length for clustered keys (r = 3, r = 9) and for keys
+      with i.i.d. Gumbel scores, whose factor / L skip has a closed form.
 
 The method and its parameters: vLLM-Omni design page "Skip-Softmax",
 sections "The threshold" and "Timestep gating"; BLASST summary page, section
@@ -90,7 +96,7 @@ def rel_l2_gpu(a: torch.Tensor, b: torch.Tensor) -> float:
 def md_table(rows, cols) -> str:
     out = ["| " + " | ".join(cols) + " |", "|" + "---|" * len(cols)]
     for r in rows:
-        out.append("| " + " | ".join(str(r.get(c, "")) for c in cols) + " |")
+        out.append("| " + " | ".join("" if r.get(c) is None else str(r[c]) for c in cols) + " |")
     return "\n".join(out)
 
 
@@ -453,8 +459,88 @@ def run_paged(args):
     return rows, cols
 
 
+# --------------------------------------------------------------------------- stability
+
+def gumbel_closed_form_skip(L: int, a: float, tk: int = 128) -> float:
+    """Expected skip fraction of one streaming pass over L keys with i.i.d.
+    standard-Gumbel scaled scores at threshold a / L: the running max before
+    tile j+1 is ln(tk j) plus a Gumbel draw, the tile max ln(tk) plus another,
+    their difference is logistic, so tile j+1 is skipped with probability
+    a j / (a j + L); the first tile never is."""
+    n = L // tk
+    j = np.arange(1, n)
+    return float((a * j / (a * j + L)).sum() / n)
+
+
+def run_stability(args):
+    from synth import WORKLOADS, gumbel_decode, make_inputs
+
+    timer, rows = Timer(), []
+    base = WORKLOADS["gqa_decode_32k"]
+    ctxs = [4096, 8192, 16384, 32768, 65536, 131072, 204800]
+    for dist in ("clustered r=3", "clustered r=9", "gumbel"):
+        data = {}
+        for L in ctxs:
+            B = max(1, min(64, (1 << 30) // (L * base.Hkv * base.D * 2)))
+            seed = base.seed + 10 + ctxs.index(L)
+            t = time.time()
+            if dist == "gumbel":
+                w = base.replace(B=B, Lk=L, seed=seed)
+                x = gumbel_decode(seed, B, w.Hq, w.Hkv, L, w.D, w.Dv, w.scale)
+            else:
+                w = base.replace(B=B, Lk=L, r=float(dist[-1]), seed=seed)
+                x = make_inputs(w)
+            q, k, v = (x[n].cuda() for n in "qkv")
+            del x
+            ws = torch.empty(ss_attn_decode_workspace_bytes(B, w.Hq, w.Hkv, L, w.D, w.Dv, 0),
+                             dtype=torch.uint8, device="cuda")
+            mask = torch.empty(mask_shape_decode(B, w.Hkv, L), dtype=torch.uint8, device="cuda")
+            out = torch.empty((B, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda")
+            log(f"[stability] {dist} L={L} B={B} generated in {time.time() - t:.1f}s")
+
+            def call(thr, q=q, k=k, v=v, ws=ws, mask=mask, out=out, w=w):
+                ss_attn_decode_partial(q, k, v, scale=w.scale, threshold=thr, skip_mask=mask,
+                                       workspace=ws)
+                ss_attn_decode_combine(q, k, ws, out, v=v)
+
+            def skip_at(thr, call=call, mask=mask):
+                call(thr)
+                torch.cuda.synchronize()
+                return skip_fraction(mask)
+
+            data[L] = (B, call, skip_at)
+        for tgt in (0.7, 0.9):
+            t32, s32, reach = bisect_threshold(data[32768][2], tgt, iters=30, tol=0.003)
+            factor = t32 * 32768
+            emit({"keys": dist, "target": tgt, "stage": "calibrated at 32K",
+                  "threshold": float(f"{t32:.6g}"), "factor": float(f"{factor:.6g}"),
+                  "skip": round(s32, 4), "reachable": reach}, rows)
+            for L in ctxs:
+                B, call, skip_at = data[L]
+                thr_a = ss_resolve_threshold("direct", threshold=factor / L, seqlen=L)
+                s_fixed = skip_at(t32)
+                s_scaled = skip_at(thr_a)
+                dense_ms = timer.ms(lambda: call(0.0), iters=7)
+                ms = timer.ms(lambda: call(thr_a), iters=7)
+                closed = (round(gumbel_closed_form_skip(L, factor), 4) if dist == "gumbel"
+                          else None)
+                emit({"keys": dist, "target": tgt, "L": L, "B": B,
+                      "skip_fixed_threshold": round(s_fixed, 4),
+                      "skip_factor_over_L": round(s_scaled, 4),
+                      "closed_form_factor_over_L": closed,
+                      "threshold_factor_over_L": float(f"{thr_a:.6g}"),
+                      "dense_ms": round(dense_ms, 4), "ms": round(ms, 4),
+                      "speedup": round(dense_ms / ms, 3)}, rows)
+        del data
+        torch.cuda.empty_cache()
+    cols = ["keys", "target", "stage", "L", "B", "threshold", "factor", "skip", "reachable",
+            "skip_fixed_threshold", "skip_factor_over_L", "closed_form_factor_over_L",
+            "threshold_factor_over_L", "dense_ms", "ms", "speedup"]
+    return rows, cols
+
+
 RUNS = {"prefill": run_prefill_sweep, "video": run_video, "latent": run_latent,
-        "decode": run_decode, "paged": run_paged}
+        "decode": run_decode, "paged": run_paged, "stability": run_stability}
 
 
 def main(argv=None):

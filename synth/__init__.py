@@ -11,6 +11,7 @@ from .generators import (  # noqa: F401
     bf16_round,
     clustered_decode,
     clustered_prefill,
+    gumbel_decode,
     video_dit_field,
 )
 from .workloads import WORKLOADS, Workload, make_inputs  # noqa: F401

@@ -9,7 +9,7 @@ for bf16 workloads, rounded once to bf16 with round-to-nearest-even (torch's
 CPU cast).  Whatever consumes the tensors (the fp64 oracle, the GPU kernels)
 reads back exactly those rounded values.
 
-Two families:
+Three families:
 
 * ``clustered_*`` -- keys sit near unit-norm centroids, one centroid per
   128-key tile, so a query near a few centroids scores high on a few tiles and
@@ -19,6 +19,10 @@ Two families:
   fields over a (frames, height, width) latent grid plus a bounded locality
   term, so nearby tokens score high: a stand-in for video diffusion
   transformer self-attention.
+* ``gumbel_decode`` -- every head of a KV group shares one query direction
+  ``u`` and each key's component along ``u`` is chosen so that the scaled
+  score ``scale * q.k`` is an independent standard Gumbel draw: a control
+  workload whose score statistics are known in closed form at any length.
 """
 
 from __future__ import annotations
@@ -260,3 +264,38 @@ def paged_decode(seed: int, lens, Hq: int, Hkv: int, D: int, Dv: int, n_c: int, 
             "block_table": torch.from_numpy(table), "seq_lens": torch.tensor(lens, dtype=torch.int32),
             "k_seqs": [s_["k"][0] for s_ in seqs], "v_seqs": [s_["v"][0] for s_ in seqs]}
 
+
+
+def gumbel_decode(seed: int, B: int, Hq: int, Hkv: int, Lk: int, D: int, Dv: int, scale: float,
+                  dtype: str = "bf16") -> dict:
+    """Decode inputs whose scaled scores are i.i.d. standard Gumbel.
+
+    Draw order, from the stream of each (b, kv head): the direction ``u``
+    (normal, normalised), the scores ``g ~ Gumbel(0, 1)`` [Lk], the key noise
+    [Lk, D] (projected off ``u``), then V [Lk, Dv].  Every query head of the
+    group is ``q = u``; key ``i`` is ``(g_i / scale) * u + noise_i``, so
+    ``scale * q.k_i = g_i`` up to the rounding of the stored values.  With
+    ``dtype="bf16"`` the rounding moves a score by a few hundredths, with
+    ``"f32"`` by ~1e-6.
+    """
+    g_ = Hq // Hkv
+    tdt = _torch_dtype(dtype)
+    q = torch.empty((B, Hq, D), dtype=tdt)
+    k = torch.empty((B, Hkv, Lk, D), dtype=tdt)
+    v = torch.empty((B, Hkv, Lk, Dv), dtype=tdt)
+
+    def unit(bh):
+        b, hk = bh
+        rng = _unit_rng(seed, b, hk)
+        u = rng.standard_normal(D)
+        u /= np.linalg.norm(u)
+        g = rng.gumbel(size=Lk)
+        noise = rng.standard_normal((Lk, D))
+        noise -= np.outer(noise @ u, u)
+        kk = (g / scale)[:, None] * u[None, :] + noise
+        q[b, hk * g_:(hk + 1) * g_] = _to_tensor(np.repeat(u[None, :], g_, axis=0), dtype)
+        k[b, hk] = _to_tensor(kk, dtype)
+        v[b, hk] = _to_tensor(rng.standard_normal((Lk, Dv), dtype=np.float32), dtype)
+
+    _for_units([(b, hk) for b in range(B) for hk in range(Hkv)], unit)
+    return {"q": q, "k": k, "v": v}

@@ -40,6 +40,7 @@ MUTATIONS = {
     "wrong tile of a key": ("keys = np.arange(j * tk, min((j + 1) * tk, Lk))",
                             "keys = np.arange(j * tk, min((j + 1) * tk + 1, Lk))"),
     "natural-log threshold replaced by log10": ("math.log(thr)", "math.log10(thr)"),
+    "natural-log threshold replaced by log2": ("math.log(thr)", "math.log2(thr)"),
 }
 
 
@@ -68,6 +69,7 @@ def battery():
     yield pins.test_visit_orders
     yield pins.test_split_ranges
     yield pins.test_uniform_skips_only_where_every_row_skips
+    yield lambda: pins.test_gumbel_scores_skip_fraction_matches_closed_form(4096, 64.0, 128)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))

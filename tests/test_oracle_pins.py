@@ -19,7 +19,7 @@ import pytest
 from scipy.special import softmax
 
 import oracle
-from synth import clustered_decode, clustered_prefill
+from synth import clustered_decode, clustered_prefill, gumbel_decode
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -345,6 +345,42 @@ def test_skip_is_monotone_in_threshold():
         if prev is not None:
             assert np.all(m >= prev)
         prev = m
+
+
+def gumbel_expected_skip(L, a, tk=128):
+    """Expected skip fraction of one streaming pass over ``L`` keys whose
+    scaled scores are i.i.d. standard Gumbel, at threshold ``a / L``.
+
+    The maximum of n i.i.d. Gumbel(0, 1) draws is ln n + Gumbel(0, 1) (the
+    family is max-stable), so before tile j+1 (j full tiles seen) the running
+    max is ln(tk j) + G1 and the tile max is ln(tk) + G2, with G1 and G2
+    independent.  G1 - G2 is logistic, and exp(tile max - running max) < a / L
+    holds with probability a j / (a j + L).  Tile 1 is never skipped.  The
+    sum over tiles depends on L only through the tile count, so for a fixed
+    ``a`` the skip fraction is (up to a 1/n term) the same at every length:
+    the threshold scaling 1/L keeps sparsity stable exactly when scores have
+    this unit exponential tail.
+    """
+    n = L // tk
+    j = np.arange(1, n)
+    return float((a * j / (a * j + L)).sum() / n)
+
+
+@pytest.mark.parametrize("L,a,streams", [(4096, 3000.0, 96), (8192, 900.0, 96),
+                                         (4096, 64.0, 128)])
+def test_gumbel_scores_skip_fraction_matches_closed_form(L, a, streams):
+    """Sample mean of the per-stream skip fraction within 4 standard errors
+    of the closed form (threshold a/L scaled by the sequence length, the
+    BLASST summary page, "Calibratie en Thresholding")."""
+    D = 64
+    B, Hkv = streams // 4, 4
+    x = gumbel_decode(81 + L, B, Hkv, Hkv, L, D, 16, 1 / math.sqrt(D), dtype="f32")
+    q, k, v = (oracle.to_f64(x[n]) for n in "qkv")
+    mask = oracle.decode(q, k, v, 1 / math.sqrt(D), a / L, 1)["mask"]
+    per_stream = (mask == 1).mean(axis=2).ravel()
+    se = per_stream.std(ddof=1) / math.sqrt(per_stream.size)
+    want = gumbel_expected_skip(L, a)
+    assert abs(per_stream.mean() - want) <= 4 * se, (per_stream.mean(), want, se)
 
 
 def test_split_refinement_only_shrinks_skip_set():
