@@ -14,8 +14,10 @@ decode's algorithmic bytes (K, plus V of the kept tiles, plus q and out) per
 second of step wall time.  The causal GQA prefill (B1, Hq32/Hkv8, L16384,
 D128) is timed in the same run and reported under ``prefill``.
 
-Every timed step is preceded by a rewrite of a 1 GiB buffer, so no step finds
-K/V in L2 or in the 256 MB last-level cache; the step and its kernels are
+Every timed step is preceded by a read of a 1 GiB buffer, so no step finds
+K/V in L2 or in the 256 MB last-level cache (a read, not a rewrite: a rewrite
+leaves dirty lines whose write-back to HBM would land inside the timed step);
+the step and its kernels are
 timed with HIP events on the stream they run on, and ``value`` uses the mean
 of those step times.  ``warm_value`` is the same decode run back to back
 (wall clock over the steps, caches left as the previous step left them).
@@ -114,14 +116,14 @@ def bench_decode(ss, torch, args):
 
     def timed(th, steps, warmup):
         """(step ms, decode kernel ms, combine ms) over `steps` cold steps, each
-        after a cache-evicting rewrite; plus the warm wall-clock step ms."""
+        after a cache-evicting read; plus the warm wall-clock step ms."""
         for _ in range(warmup):
             partial(th)
             combine()
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         for i, e in enumerate(evs):
-            args.flush.fill_(i & 255)
+            evict_caches(args.flush)
             e[0].record()
             partial(th)
             e[1].record()
@@ -197,7 +199,7 @@ def bench_prefill(ss, torch, args, r, order):
         steps = max(5, args.steps // 2)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for i, e in enumerate(evs):
-            args.flush.fill_(i & 255)
+            evict_caches(args.flush)
             e[0].record()
             run(th)
             e[1].record()
@@ -258,7 +260,7 @@ def bench_latent(ss, torch, args):
         steps = max(5, args.steps // 4)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for i, e in enumerate(evs):
-            args.flush.fill_(i & 255)
+            evict_caches(args.flush)
             e[0].record()
             call(th)
             e[1].record()
@@ -310,6 +312,14 @@ def cpu_baseline(dec, seconds):
 
 
 # --------------------------------------------------------------------------- main
+
+def evict_caches(buf):
+    """Push K/V out of L2 and the last-level cache before a timed call by
+    READING a 1 GiB buffer.  Rewriting it (fill_) would leave up to the cache's
+    size of dirty lines behind, and their write-back to HBM would then be
+    charged to the next timed call."""
+    buf.max()
+
 
 def copy_probe(torch):
     n = 1 << 30
@@ -369,7 +379,7 @@ def main():
         return
     if args.only_sparse_decode:
         args.no_prefill = args.no_cpu = args.no_latent = True
-    args.flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    args.flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
 
     dec = bench_decode(ss, torch, args)
     w, by = dec["workload"], dec["bytes"]

@@ -66,18 +66,19 @@ def log(*a):
 
 
 class Timer:
-    """Median per-call time in ms, with L2 and last-level cache evicted
-    before every call."""
+    """Median per-call time in ms, with L2 and the last-level cache evicted
+    before every call by reading a 1 GiB buffer (a rewrite would leave dirty
+    lines whose write-back lands in the timed call)."""
 
     def __init__(self, flush_bytes: int = 1 << 30):
-        self.flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+        self.flush = torch.ones(flush_bytes, dtype=torch.uint8, device="cuda")
 
     def ms(self, fn, iters: int = 15, warmup: int = 3) -> float:
         for _ in range(warmup):
             fn()
         ts = []
         for i in range(iters):
-            self.flush.fill_(i & 255)
+            self.flush.max()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()

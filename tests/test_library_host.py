@@ -123,9 +123,11 @@ def test_threshold_rejects_bad_domain(ss):
 
 def test_split_policy_is_deterministic_and_bounded(ss):
     # GQA decode, Llama-3.1-8B attention shape at 32K: 128 (batch, kv head)
-    # units x 256 tiles -> 16 tiles per split (the chained capacity for a group
-    # of 4), 16 splits, 2048 workgroups
-    assert ss.ss_decode_num_splits(16, 32, 8, 32768, 128, 128) == 16
+    # units x 256 tiles, ~2816 workgroups wanted -> 12 tiles per split
+    # (within the chained capacity of 16 for a group of 4), 22 splits
+    assert ss.ss_decode_num_splits(16, 32, 8, 32768, 128, 128) == 22
+    # at 200K keys the chained capacity binds: 16 tiles per split
+    assert ss.ss_decode_num_splits(16, 32, 8, 204800, 128, 128) == 100
     # small problems: one tile per split
     assert ss.ss_decode_num_splits(1, 4, 2, 1000, 128, 128) == 8
     # group of 1: capacity 64 tiles
