@@ -22,6 +22,7 @@ __all__ = [
     "ss_attn_decode_workspace_bytes", "ss_decode_num_splits", "ss_factor", "ss_threshold",
     "ss_gate_enabled", "ss_resolve_threshold", "ss_last_error", "ss_version", "library_path",
     "SSError", "TILE", "ORDERS", "mask_shape_prefill", "mask_shape_decode",
+    "ss_attn_decode_paged", "GRANULARITIES", "row_mask_shape_prefill", "row_mask_shape_decode",
 ]
 
 TILE = 128
@@ -50,7 +51,8 @@ class _PrefillParams(ctypes.Structure):
                 ("Hkv", ctypes.c_int), ("Lq", ctypes.c_int), ("Lk", ctypes.c_int),
                 ("D", ctypes.c_int), ("Dv", ctypes.c_int), ("scale", ctypes.c_float),
                 ("threshold", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
-                ("order", ctypes.c_int), ("skip_mask_out", ctypes.c_void_p)]
+                ("order", ctypes.c_int), ("skip_mask_out", ctypes.c_void_p),
+                ("granularity", ctypes.c_int), ("row_mask_out", ctypes.c_void_p)]
 
 
 class _DecodeParams(ctypes.Structure):
@@ -60,7 +62,8 @@ class _DecodeParams(ctypes.Structure):
                 ("Dv", ctypes.c_int), ("scale", ctypes.c_float), ("threshold", ctypes.c_float),
                 ("num_splits", ctypes.c_int), ("split_mode", ctypes.c_int),
                 ("skip_mask_out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("granularity", ctypes.c_int),
+                ("row_mask_out", ctypes.c_void_p)]
 
 
 class _DecodePagedParams(ctypes.Structure):
@@ -77,6 +80,8 @@ class _DecodePagedParams(ctypes.Structure):
 
 
 SPLIT_MODES = {"chained": 0, "independent": 1}
+# who takes a skip decision: the whole row block of a tile, or every row alone
+GRANULARITIES = {"tile": 0, "row": 1}
 
 _LIB = None
 
@@ -159,14 +164,37 @@ def mask_shape_decode(B, Hkv, Lk):
     return (B, Hkv, -(-Lk // TILE))
 
 
+def row_mask_shape_prefill(B, Hq, Lq, Lk):
+    return (B, Hq, Lq, -(-Lk // TILE))
+
+
+def row_mask_shape_decode(B, Hq, Lk):
+    return (B, Hq, -(-Lk // TILE))
+
+
+def _granularity(granularity, row_mask, shape):
+    if granularity not in GRANULARITIES:
+        raise ValueError(f"granularity must be one of {sorted(GRANULARITIES)}")
+    if row_mask is None:
+        return GRANULARITIES[granularity], None
+    if granularity != "row":
+        raise ValueError("row_mask needs granularity='row'")
+    if tuple(row_mask.shape) != shape:
+        raise ValueError(f"row_mask must be {shape}")
+    return GRANULARITIES[granularity], _dev(row_mask, "row_mask", torch.uint8)
+
+
 # --------------------------------------------------------------------------- prefill
 
 def ss_attn_prefill_ex(q, k, v, out=None, *, scale=None, causal=False, threshold=0.0,
-                       skip_mask=None, order="ascending", stream=None):
+                       skip_mask=None, order="ascending", granularity="tile", row_mask=None,
+                       stream=None):
     """Skip-softmax prefill: q[B,Hq,Lq,D], k[B,Hkv,Lk,D], v[B,Hkv,Lk,Dv] on the GPU
     (all bf16 or all fp32).  Returns ``out`` [B,Hq,Lq,Dv]; fills ``skip_mask``
-    (u8 [B,Hq,ceil(Lq/128),ceil(Lk/128)]) when given.  Asynchronous on
-    ``stream`` (default: the current stream)."""
+    (u8 [B,Hq,ceil(Lq/128),ceil(Lk/128)]) when given.  ``granularity="row"``
+    lets every query row decide alone; ``row_mask`` (u8
+    [B,Hq,Lq,ceil(Lk/128)]) then receives the per-row decisions.  Asynchronous
+    on ``stream`` (default: the current stream)."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, L, D]")
     B, Hq, Lq, D = q.shape
@@ -190,9 +218,10 @@ def ss_attn_prefill_ex(q, k, v, out=None, *, scale=None, causal=False, threshold
         scale = 1.0 / math.sqrt(D)
     if order not in ORDERS:
         raise ValueError(f"order must be one of {sorted(ORDERS)}")
+    gran, rptr = _granularity(granularity, row_mask, row_mask_shape_prefill(B, Hq, Lq, Lk))
     p = _PrefillParams(_dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _dev(out, "out", dt),
                        B, Hq, Hkv, Lq, Lk, D, Dv, float(scale), float(threshold), int(bool(causal)),
-                       _DTYPE[dt], ORDERS[order], mptr)
+                       _DTYPE[dt], ORDERS[order], mptr, gran, rptr)
     _check(lib().ss_attn_prefill_ex(ctypes.byref(p), _stream(stream, q.device)))
     return out
 
@@ -226,7 +255,7 @@ def ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits=0) -> int:
 
 
 def _decode_params(q, k, v, out, dv, scale, threshold, num_splits, split_mode, skip_mask,
-                   workspace):
+                   workspace, granularity="tile", row_mask=None):
     if q.dim() != 3 or k.dim() != 4:
         raise ValueError("q must be [B, Hq, D] and k [B, Hkv, Lk, D]")
     B, Hq, D = q.shape
@@ -256,19 +285,21 @@ def _decode_params(q, k, v, out, dv, scale, threshold, num_splits, split_mode, s
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    gran, rptr = _granularity(granularity, row_mask, row_mask_shape_decode(B, Hq, Lk))
     p = _DecodeParams(_dev(q, "q", dt), _dev(k, "k", dt), vptr,
                       None if out is None else _dev(out, "out", dt), B, Hq, Hkv, Lk, D, Dv,
                       float(scale), float(threshold), int(num_splits), SPLIT_MODES[split_mode],
                       mptr, _dev(workspace, "workspace"),
-                      workspace.numel() * workspace.element_size())
+                      workspace.numel() * workspace.element_size(), gran, rptr)
     return p, workspace, (B, Hq, Dv)
 
 
 def ss_attn_decode_partial(q, k, v=None, *, dv=None, scale=None, threshold=0.0, num_splits=0,
-                           split_mode="chained", skip_mask=None, workspace=None, stream=None):
+                           split_mode="chained", skip_mask=None, workspace=None,
+                           granularity="tile", row_mask=None, stream=None):
     """First stage of the decode: run every split into ``workspace`` (returned)."""
     p, ws, _ = _decode_params(q, k, v, None, dv, scale, threshold, num_splits, split_mode,
-                              skip_mask, workspace)
+                              skip_mask, workspace, granularity, row_mask)
     _check(lib().ss_attn_decode_partial(ctypes.byref(p), _stream(stream, q.device)))
     return ws
 
@@ -284,19 +315,21 @@ def ss_attn_decode_combine(q, k, workspace, out, *, v=None, dv=None, num_splits=
 
 def ss_attn_decode_ex(q, k, v=None, out=None, *, dv=None, scale=None, threshold=0.0,
                       num_splits=0, split_mode="chained", skip_mask=None, workspace=None,
-                      stream=None):
+                      granularity="tile", row_mask=None, stream=None):
     """Split-KV skip-softmax decode: q[B,Hq,D], k[B,Hkv,Lk,D], v[B,Hkv,Lk,Dv] bf16,
     or ``v=None`` with ``dv`` for a latent cache whose value rows are the first
     ``dv`` columns of each key row.  Returns ``out`` [B,Hq,Dv]; fills
     ``skip_mask`` (u8 [B,Hkv,ceil(Lk/128)]) when given.  ``split_mode``:
     "chained" (decisions of one streaming pass) or "independent" (each split
     restarts the running max).  ``workspace``: a uint8 GPU tensor of at least
-    ss_attn_decode_workspace_bytes() bytes (allocated here when None)."""
+    ss_attn_decode_workspace_bytes() bytes (allocated here when None).
+    ``granularity="row"`` lets every query head decide alone (separate V only);
+    ``row_mask`` (u8 [B,Hq,ceil(Lk/128)]) then receives the per-row decisions."""
     if out is None:
         Dv = int(dv) if v is None else v.shape[3]
         out = torch.empty((q.shape[0], q.shape[1], Dv), dtype=torch.bfloat16, device=q.device)
     p, _, _ = _decode_params(q, k, v, out, dv, scale, threshold, num_splits, split_mode,
-                             skip_mask, workspace)
+                             skip_mask, workspace, granularity, row_mask)
     _check(lib().ss_attn_decode_ex(ctypes.byref(p), _stream(stream, q.device)))
     return out
 

@@ -198,6 +198,14 @@ unsigned next_tag() {
   return t | 1u;
 }
 
+int check_granularity(int granularity, const uint8_t* row_mask_out) {
+  if (granularity != SS_SKIP_TILE && granularity != SS_SKIP_ROW)
+    return fail(SS_ERR_INVALID_ARG, "unknown granularity %d", granularity);
+  if (row_mask_out && granularity != SS_SKIP_ROW)
+    return fail(SS_ERR_INVALID_ARG, "row_mask_out needs granularity SS_SKIP_ROW");
+  return SS_OK;
+}
+
 int validate_prefill(const ss_prefill_params* p) {
   if (!p) return fail(SS_ERR_INVALID_ARG, "params is null");
   if (!p->q || !p->k || !p->v || !p->out)
@@ -224,6 +232,7 @@ int validate_prefill(const ss_prefill_params* p) {
   } else {
     return fail(SS_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
   }
+  if (int rc = check_granularity(p->granularity, p->row_mask_out)) return rc;
   return SS_OK;
 }
 
@@ -237,7 +246,7 @@ const char* ss_version(void) { return "ssattn 0.1.0 (gfx950)"; }
 
 int ss_attn_prefill_ex(const ss_prefill_params* p, hipStream_t stream) {
   if (int rc = validate_prefill(p)) return rc;
-  ssattn::PrefillArgs a;
+  ssattn::PrefillArgs a{};
   a.q = p->q;
   a.k = p->k;
   a.v = p->v;
@@ -255,6 +264,8 @@ int ss_attn_prefill_ex(const ss_prefill_params* p, hipStream_t stream) {
   a.thr_above_1 = p->threshold > 1.f;
   a.causal = p->causal != 0;
   a.order = p->order;
+  a.per_row = p->granularity == SS_SKIP_ROW;
+  a.row_mask = p->row_mask_out;
   hipError_t e = p->dtype == SS_DTYPE_BF16 ? ssattn::launch_prefill_bf16(a, stream)
                                            : ssattn::launch_prefill_f32(a, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
@@ -327,6 +338,9 @@ int prepare_decode(const ss_decode_params* p, bool stage_partial, ssattn::Decode
     return fail(SS_ERR_UNSUPPORTED, "no decode kernel for D=%d Dv=%d group=%d %s", p->D, p->Dv,
                 group, latent ? "(latent V)" : "(separate V)");
   *kernel = k;
+  if (int rc = check_granularity(p->granularity, p->row_mask_out)) return rc;
+  if (stage_partial && p->granularity == SS_SKIP_ROW && k != DecodeKernel::kGqa)
+    return fail(SS_ERR_UNSUPPORTED, "per-row skip decisions need the separate-V decode");
   const bool chained = p->split_mode == SS_SPLIT_CHAINED;
   const DecodePlan pl = plan_decode(p->B, p->Hq, p->Hkv, p->Lk, p->D, p->Dv,
                                     k == DecodeKernel::kMla, p->num_splits, chained);
@@ -359,6 +373,8 @@ int prepare_decode(const ss_decode_params* p, bool stage_partial, ssattn::Decode
   a->log2_thr = log2_threshold(p->threshold);
   a->thr_above_1 = p->threshold > 1.f;
   a->lb_tag = 0;
+  a->per_row = p->granularity == SS_SKIP_ROW;
+  a->row_mask = p->row_mask_out;
   return SS_OK;
 }
 

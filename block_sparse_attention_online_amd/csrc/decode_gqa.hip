@@ -21,7 +21,9 @@
 //  2. Decision.  One wave scans the chunk's tile maxima: lane t holds tile t,
 //     an exclusive prefix max over lanes gives every tile its running max, and
 //     the tile is skipped iff max over rows of (tile_max - running_max) <
-//     log2(threshold).  Kept tiles are compacted into a survivor list.
+//     log2(threshold).  Kept tiles are compacted into a survivor list.  With
+//     per-row decisions the tile is kept under the same rule (some row passes)
+//     and each kept tile also records which rows passed; the others get P = 0.
 //     Every sub-split first publishes its local maxima and reads those of the
 //     earlier sub-splits of its chain, so the decisions are exactly those of
 //     one streaming pass over the chain; the sub-splits still run in parallel
@@ -68,6 +70,7 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
   __shared__ float s_mref[G];
   __shared__ float s_lred[kWaves][G];
   __shared__ int s_surv[TMAX];
+  __shared__ unsigned s_rowkeep[TMAX];  // per kept tile: bit r = row r adds its P
   __shared__ int s_nsurv;
   __shared__ int s_blk[PAGED ? TMAX * kTile / 16 : 1];  // paged: this sub-split's cache blocks
 
@@ -280,6 +283,7 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
     // running max before each tile: earlier links, then an exclusive prefix
     // max over this link's tiles (lane t = tile t)
     float dmax = neg_inf();
+    unsigned rowkeep = 0;  // bit r: row r passes its own test on this lane's tile
 #pragma unroll
     for (int r = 0; r < G; ++r) {
       const float mstart = lanes_max_from<1>(prev[r]);
@@ -295,12 +299,21 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
       float dr = neg_inf();
       if (tm[r] != neg_inf()) dr = (M == neg_inf()) ? pos_inf() : tm[r] - M;
       dmax = fmaxf(dmax, dr);
+      if (!(dr < log2_thr)) rowkeep |= 1u << r;
     }
     const bool skip = dmax < log2_thr;
     const bool kept = valid && !skip;
     const unsigned long long bits = __ballot(kept);
     const int idx = __popcll(bits & ((1ull << lane) - 1ull));
     if (kept) s_surv[idx] = lane;
+    if constexpr (!PAGED) {
+      if (valid) s_rowkeep[lane] = a.per_row ? rowkeep : 0xffu;
+      if (valid && a.row_mask) {
+#pragma unroll
+        for (int r = 0; r < G; ++r)
+          a.row_mask[((size_t)b * a.Hq + hk * G + r) * nK + t0 + lane] = (rowkeep >> r) & 1u ? 0 : 1;
+      }
+    }
     if (lane == 0) s_nsurv = __popcll(bits);
     if (valid && a.mask)
       a.mask[(size_t)pair * (PAGED ? a.mask_tiles : nK) + t0 + lane] = skip ? 1 : 0;
@@ -334,6 +347,12 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
     };
     auto accum_v = [&](int si, const u32x4_t (&src)[IT]) {
       const int tl = s_surv[si];
+      // rows that did not pass on this tile (per-row decisions) take +inf as
+      // their exponent reference: P = 0
+      const unsigned keep = PAGED ? 0xffu : s_rowkeep[tl];
+      float mx[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) mx[r] = (keep >> r) & 1u ? mref[r] : pos_inf();
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int kin = w * kKeysPerWave + it * KPI + kq;
@@ -342,10 +361,10 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
         if constexpr (G == 4) {
           const f4_t s4 = *reinterpret_cast<const f4_t*>(srow);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s4[r] - mref[r]);
+          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s4[r] - mx[r]);
         } else {
 #pragma unroll
-          for (int r = 0; r < G; ++r) p[r] = fast_exp2(srow[r] - mref[r]);
+          for (int r = 0; r < G; ++r) p[r] = fast_exp2(srow[r] - mx[r]);
         }
         float vf[8];
 #pragma unroll

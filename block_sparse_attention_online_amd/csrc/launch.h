@@ -22,6 +22,10 @@ struct PrefillArgs {
   int thr_above_1;  // threshold > 1: a skipped tile may raise m
   int causal;
   int order;  // ss_order
+  // Per-row decisions: rows that fail the test add nothing from a kept tile;
+  // row_mask (may be null) is u8 [B, Hq, Lq, nK].
+  int per_row;
+  uint8_t* row_mask;
 };
 
 // Arguments of one split-KV decode launch.
@@ -61,6 +65,10 @@ struct DecodeArgs {
   int max_blocks;
   int num_blocks;
   int mask_tiles;
+  // Per-row decisions (contiguous GQA decode): rows that fail the test add
+  // nothing from a kept tile; row_mask (may be null) is u8 [B, Hq, nK].
+  int per_row;
+  uint8_t* row_mask;
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);

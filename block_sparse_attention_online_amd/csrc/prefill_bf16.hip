@@ -36,6 +36,9 @@
 //    the wave's 32 rows by DPP, the max over the head's 4 waves through LDS;
 //    skip when it is below log2(threshold).  The branch is uniform over the
 //    head's waves, so a skipped tile issues no exp and no P.V MFMA at all.
+//    With per-row decisions the tile is still skipped exactly when every row
+//    fails the test; in a kept tile a row that fails it takes +inf as its
+//    exponent reference, so its P is 0 and it adds nothing.
 
 #include "device_common.h"
 #include "launch.h"
@@ -115,6 +118,12 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   const bool mask_writer = mrow && wr == 0;
   if (mask_writer && plan.causal)
     for (int j = plan.last + 1 + lane; j < nK; j += 64) mrow[j] = 2;
+  // per-row decisions: this lane's row of the row mask (lane half 0 writes)
+  uint8_t* const rrow = (a.row_mask && g == 0 && row_ok)
+                            ? a.row_mask + ((size_t)(b * a.Hq + head) * a.Lq + rq) * nK
+                            : nullptr;
+  if (rrow && plan.causal)
+    for (int j = plan.last + 1; j < nK; ++j) rrow[j] = 2;
 
   // Issue the direct-to-LDS loads of tile j into ring stage st.  Wave w covers
   // rows [w * LOADS * ROWS_PER_LOAD, ...); lane l of load i writes LDS row
@@ -248,6 +257,8 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
 
     float delta = neg_inf();
     if (row_ok && tmax2 != neg_inf()) delta = (m2 == neg_inf()) ? pos_inf() : tmax2 - m2;
+    const bool row_skip = delta < a.log2_thr;  // this row's own test
+    if (rrow) rrow[j] = row_skip ? 1 : 0;
     delta = wave_max(delta);
     if (lane == 0) red[hh][wr] = delta;
     __syncthreads();  // red[] visible
@@ -260,6 +271,8 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     const float m2n = fmaxf(m2, tmax2);
     if (!skip) {
       const float mref = (m2n == neg_inf()) ? 0.f : m2n;
+      // per-row decisions: a row that failed its own test gets P = 0
+      const float mexp = (a.per_row && row_skip) ? pos_inf() : mref;
       // rescale only when some row's running max grew (the factor is exactly
       // 1 for every other row)
       if (__builtin_amdgcn_ballot_w64(m2n != m2) != 0) {
@@ -293,8 +306,8 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
           unsigned int pw[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e], c, -mref));
-            const float p1 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e + 1], c, -mref));
+            const float p0 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e], c, -mexp));
+            const float p1 = fast_exp2(fmaf(sacc[kb][half * 8 + 2 * e + 1], c, -mexp));
             lpart += p0 + p1;
             pw[e] = pack_bf16x2(p0, p1);
           }

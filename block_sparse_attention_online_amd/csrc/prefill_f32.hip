@@ -6,7 +6,8 @@
 // pass" (per-row running max m, denominator l, numerator O, rescaled when m
 // grows) and "The skip test" (skip a tile when exp(tile_max - running_max) <
 // threshold; it adds nothing to l or O).  The decision is uniform over the
-// 128 rows of a query tile.
+// 128 rows of a query tile, or (per-row mode) each row decides alone and a
+// row that fails its own test adds nothing from a kept tile.
 //
 // One workgroup per (batch, query head, 128-row query tile); 256 threads:
 // thread t owns query row t % 128 and half t / 128 of the value columns.  The
@@ -54,6 +55,13 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
     }
   }
 
+  // per-row decisions: this thread's row of the row mask (half 0 writes)
+  uint8_t* const rrow = (a.row_mask && half == 0 && row_ok)
+                            ? a.row_mask + ((size_t)(b * a.Hq + h) * a.Lq + row) * nK
+                            : nullptr;
+  if (rrow && plan.causal)
+    for (int j = plan.last + 1; j < nK; ++j) rrow[j] = 2;
+
   float q[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) q[d] = row_ok ? qp[(size_t)row * D + d] : 0.f;
@@ -89,6 +97,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
     }
     float delta = neg_inf();
     if (row_ok && nvis > 0) delta = (m2 == neg_inf()) ? pos_inf() : tmax - m2;
+    const bool row_skip = delta < a.log2_thr;  // this row's own test
+    if (rrow) rrow[j] = row_skip ? 1 : 0;
     delta = lanes_max_from<1>(delta);
     if ((tid & 63) == 0) red[tid >> 6] = delta;
     __syncthreads();
@@ -103,7 +113,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
       l *= alpha;
 #pragma unroll
       for (int d = 0; d < DH; ++d) o[d] *= alpha;
-      for (int kr = 0; kr < nvis; ++kr) {
+      // per-row decisions: a row that failed its own test adds nothing
+      const int nacc = (a.per_row && row_skip) ? 0 : nvis;
+      for (int kr = 0; kr < nacc; ++kr) {
         float s = 0.f;
 #pragma unroll
         for (int d = 0; d < D; ++d) s = fmaf(q[d], Ks[kr][d], s);

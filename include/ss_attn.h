@@ -71,6 +71,22 @@ typedef enum { SS_ORDER_ASCENDING = 0, SS_ORDER_DIAG_FIRST = 1 } ss_order;
 
 enum { SS_MASK_COMPUTED = 0, SS_MASK_SKIPPED = 1, SS_MASK_UNVISITED = 2 };
 
+/* Who decides a skip.  The pages keep the running max per query row (design
+ * page, "The online-softmax pass") and state the test per key tile ("The
+ * skip test"); which query rows share one decision is left open.
+ *   SS_SKIP_TILE (default): one decision per (row block, key tile) -- the
+ *     128-row query tile of one head in prefill, the Hq/Hkv heads of one KV
+ *     head in decode -- taken when every row of the block passes the test.
+ *   SS_SKIP_ROW: every row decides alone: a row whose own
+ *     exp(tile_max_r - m_r) is below the threshold adds nothing from the tile
+ *     (its running max still moves).  A tile where every row skips runs no
+ *     exponentials and no P.V (decode: reads no V); those tiles, and so the
+ *     tile-level skip_mask_out, are the same as with SS_SKIP_TILE.  The
+ *     per-row decisions go to row_mask_out when given.
+ * Supported with SS_SKIP_ROW: prefill (bf16 and fp32) and the separate-V
+ * decode of ss_attn_decode_ex / ss_attn_decode_partial. */
+typedef enum { SS_SKIP_TILE = 0, SS_SKIP_ROW = 1 } ss_granularity;
+
 /* ------------------------------------------------------------------ prefill */
 
 /*
@@ -99,8 +115,10 @@ int ss_attn_prefill_f32(const float* q, const float* k, const float* v, float* o
                         int Hq, int Hkv, int Lq, int Lk, int D, int Dv, float scale, int causal,
                         float threshold, uint8_t* skip_mask_out, hipStream_t stream);
 
-/* Full form: the two calls above are this one with dtype BF16 / F32 and
- * order ASCENDING. */
+/* Full form: the two calls above are this one with dtype BF16 / F32, order
+ * ASCENDING and granularity SS_SKIP_TILE.  row_mask_out (SS_SKIP_ROW only,
+ * else it must be NULL): u8 [B, Hq, Lq, ceil(Lk/128)], every row's decision
+ * per key tile (2 for tiles its query tile does not visit), or NULL. */
 typedef struct {
   const void* q;
   const void* k;
@@ -113,6 +131,8 @@ typedef struct {
   int dtype; /* ss_dtype */
   int order; /* ss_order */
   uint8_t* skip_mask_out;
+  int granularity;       /* ss_granularity */
+  uint8_t* row_mask_out; /* SS_SKIP_ROW: u8 [B, Hq, Lq, ceil(Lk/128)] or NULL */
 } ss_prefill_params;
 
 int ss_attn_prefill_ex(const ss_prefill_params* p, hipStream_t stream);
@@ -175,6 +195,8 @@ typedef struct {
   uint8_t* skip_mask_out;
   void* workspace;
   size_t workspace_bytes;
+  int granularity;       /* ss_granularity; SS_SKIP_ROW needs a separate v */
+  uint8_t* row_mask_out; /* SS_SKIP_ROW: u8 [B, Hq, ceil(Lk/128)] or NULL */
 } ss_decode_params;
 
 int ss_attn_decode_ex(const ss_decode_params* p, hipStream_t stream);

@@ -207,14 +207,59 @@ def test_prefill_ex_rejects_unknown_order_and_dtype(ss):
     assert ss.lib().ss_attn_prefill_ex(None, None) == -1
 
 
+def test_prefill_rejects_bad_granularity(ss):
+    p = ss._PrefillParams(0x1000, 0x1000, 0x1000, 0x1000, 1, 1, 1, 128, 128, 128, 128, 0.1, 0.0,
+                          0, 0, 0, None, 7, None)
+    assert ss.lib().ss_attn_prefill_ex(ctypes.byref(p), None) == -1
+    assert "granularity" in ss.ss_last_error()
+    p.granularity, p.row_mask_out = 0, 0x1000  # a row mask needs per-row decisions
+    assert ss.lib().ss_attn_prefill_ex(ctypes.byref(p), None) == -1
+    assert "row_mask_out" in ss.ss_last_error()
+
+
+def test_struct_layouts_match_header(ss, tmp_path):
+    """Every field of the parameter structs sits at the offset the C compiler
+    gives it in include/ss_attn.h (the binding fills them by position)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("needs gcc and the HIP headers")
+    structs = {"ss_prefill_params": ss._PrefillParams, "ss_decode_params": ss._DecodeParams,
+               "ss_decode_paged_params": ss._DecodePagedParams}
+    lines = ['#include "ss_attn.h"', "#include <stdio.h>", "#include <stddef.h>",
+             "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} sizeof %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{name} {f} %zu\\n", offsetof({name}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    "-D__HIP_PLATFORM_AMD__", str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                               text=True).stdout.splitlines():
+        name, field, val = line.split()
+        got[(name, field)] = int(val)
+    for name, cls in structs.items():
+        assert got[(name, "sizeof")] == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert got[(name, f)] == getattr(cls, f).offset, (name, f)
+
+
 def decode_call(ss, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, Lk=1000, D=128, Dv=128,
-             scale=0.1, thr=0.01, S=0, mask=None, ws=FAKE, wsb=1 << 30, mode=0)
+             scale=0.1, thr=0.01, S=0, mask=None, ws=FAKE, wsb=1 << 30, mode=0, gran=0,
+             rmask=None)
     a.update(over)
-    if a["mode"] != 0:
+    if a["mode"] != 0 or a["gran"] != 0 or a["rmask"] is not None:
         p = ss._DecodeParams(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"], a["Hkv"], a["Lk"],
                              a["D"], a["Dv"], a["scale"], a["thr"], a["S"], a["mode"], a["mask"],
-                             a["ws"], a["wsb"])
+                             a["ws"], a["wsb"], a["gran"], a["rmask"])
         return ss.lib().ss_attn_decode_ex(ctypes.byref(p), None)
     return ss.lib().ss_attn_decode(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"], a["Hkv"],
                                    a["Lk"], a["D"], a["Dv"], a["scale"], a["thr"], a["S"],
@@ -228,6 +273,8 @@ def decode_call(ss, **over):
     (dict(Hq=48, Hkv=2), -2),                       # group of 24 heads
     (dict(D=96, Dv=96), -2), (dict(v=None, Dv=64), -2),
     (dict(ws=None), -4), (dict(wsb=100), -4), (dict(mode=7), -1),
+    (dict(gran=2), -1), (dict(rmask=FAKE), -1),    # row mask without per-row decisions
+    (dict(v=None, D=576, Dv=512, Hq=128, Hkv=1, gran=1), -2),  # per-row latent decode
 ])
 def test_decode_rejects_before_launch(ss, over, code):
     assert decode_call(ss, **over) == code
