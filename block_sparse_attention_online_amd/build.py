@@ -28,6 +28,10 @@ ARCH = "gfx950"
 # every rescale a read and a write.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
+# ... except where the accumulators alone fill the 256 architectural VGPRs:
+# the latent decode keeps a [512 x 32] fp32 output block per wave in the
+# accumulation registers.
+AGPR_FORM = {"decode_mla.hip"}
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 
@@ -46,7 +50,10 @@ def sources() -> list:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    flags = DEVICE_FLAGS
+    if os.path.basename(src) in AGPR_FORM:
+        flags = [f for f in DEVICE_FLAGS if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
+    cmd = [hipcc(), *COMMON, *flags, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -95,15 +95,17 @@ int chained_max_tiles(int D, int Dv, int group, bool latent) {
 // streaming, with no split longer than a chained split may be.  GQA: about 11
 // workgroups per compute unit (3 resident at a time); on the 32K Llama-shape
 // decode this measured 6 % faster at 70 % skip than 8 per unit, and anything
-// from 9 to 14 per unit within 1 %.  Latent: one resident workgroup each,
-// 2 rounds, each sub-split taking one workgroup per 64 query heads.  Chained
-// decisions do not depend on the count.
+// from 9 to 14 per unit within 1 %.  Latent: one resident workgroup per
+// compute unit, one workgroup per sub-split, one round (at 131072 keys, 8
+// sequences: 32 sub-splits of 32 tiles measured 296 us plus a 15 us merge,
+// against 318 + 26 us for two rounds; more splits cost more in the merge).
+// Chained decisions do not depend on the count.
 int auto_splits(int B, int Hq, int Hkv, int Lk, int D, int Dv, bool latent) {
   const int64_t nK = ceil_div(Lk, SS_TILE_KEYS);
   const int64_t units = (int64_t)B * Hkv;
   const int group = Hq / Hkv;
   const int64_t want = decode_kernel(D, Dv, group, latent) == DecodeKernel::kMla
-                           ? 512 / ssattn::decode_mla_workgroups_per_split(group)
+                           ? 256 / ssattn::decode_mla_workgroups_per_split(group)
                            : 11 * 256;
   int64_t per = ceil_div(nK * units, want);
   const int64_t cap = chained_max_tiles(D, Dv, Hq / Hkv, latent);
@@ -117,7 +119,7 @@ struct DecodePlan {
   int tiles_per_sub;   // tiles per sub-split
   int chain_tiles;     // tiles per chain
   int subs_per_chain;  // sub-splits per chain
-  size_t o_off, lse_off, slot_off, xchg_off, timeout_off, bytes;
+  size_t o_off, lse_off, slot_off, timeout_off, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -171,13 +173,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int Lk, int D, int Dv, bool laten
   p.o_off = 0;
   p.lse_off = align256(rows * (size_t)Dv * sizeof(float));
   p.slot_off = p.lse_off + align256(rows * sizeof(float));
-  p.xchg_off = p.slot_off + align256(slots * (size_t)(Hq / Hkv) * sizeof(unsigned long long));
-  // latent decode: the two halves of a head group exchange one value per tile
-  const size_t xchg = decode_kernel(D, Dv, Hq / Hkv, latent) == DecodeKernel::kMla
-                          ? slots * 2 * (size_t)ssattn::decode_mla_max_tiles(Hq / Hkv) *
-                                sizeof(unsigned long long)
-                          : 0;
-  p.timeout_off = p.xchg_off + align256(xchg);
+  p.timeout_off = p.slot_off + align256(slots * (size_t)(Hq / Hkv) * sizeof(unsigned long long));
   p.bytes = p.timeout_off + 256;
   return p;
 }
@@ -356,8 +352,6 @@ int prepare_decode(const ss_decode_params* p, bool stage_partial, ssattn::Decode
   a->part_o = reinterpret_cast<float*>(ws + pl.o_off);
   a->part_lse = reinterpret_cast<float*>(ws + pl.lse_off);
   a->lb_slot = reinterpret_cast<unsigned long long*>(ws + pl.slot_off);
-  a->lb_xchg = k == DecodeKernel::kMla ? reinterpret_cast<unsigned long long*>(ws + pl.xchg_off)
-                                       : nullptr;
   a->lb_timeouts = reinterpret_cast<unsigned int*>(ws + pl.timeout_off);
   a->B = p->B;
   a->Hq = p->Hq;
@@ -447,7 +441,6 @@ int ss_attn_decode_paged(const ss_decode_paged_params* p, hipStream_t stream) {
   a.part_o = reinterpret_cast<float*>(ws + pl.o_off);
   a.part_lse = reinterpret_cast<float*>(ws + pl.lse_off);
   a.lb_slot = reinterpret_cast<unsigned long long*>(ws + pl.slot_off);
-  a.lb_xchg = nullptr;
   a.lb_timeouts = reinterpret_cast<unsigned int*>(ws + pl.timeout_off);
   a.B = p->B;
   a.Hq = p->Hq;

@@ -9,32 +9,35 @@
 // against its running max.  Since the value is a slice of the key row, a
 // skipped tile saves the exponentials and the P.V product, not HBM bytes.
 //
-// Work split: one workgroup per (batch, sub-split of at most 64 tiles, half of
-// the head group); a half is 64 query heads.  4 waves; wave w owns heads
-// [16 w, 16 w + 16) of the half and the whole 128-key tile, so each wave has
-// full tiles for its heads: tile maxima, exponentials and P stay in its
-// registers.  MFMA v_mfma_f32_16x16x32_bf16 throughout; Q stays in registers
-// as the B operand for the whole call.
+// Work split: one workgroup per (batch, sub-split of at most 64 tiles) with
+// all G query heads: G / 32 waves, wave w owns heads [32 w, 32 w + 32).  MFMA
+// v_mfma_f32_32x32x16_bf16 throughout, transposed products so the heads are
+// the MFMA columns:
+//   S^T [32 keys x 32 heads] = K [32 x 576] . Q^T [576 x 32]
+//   O^T [512 x 32 heads]    += V^T [512 x 32 keys] . P^T [32 keys x 32 heads]
+// Q^T lives in registers for the whole call (36 k-steps), O^T in the
+// accumulation registers (16 blocks of 32 value columns).  The lane that owns
+// a head's scores also holds them in the layout of the P^T operand, so the
+// exponentials never leave the lane.  The decision (a max over heads) crosses
+// waves through LDS once per sub-split; no other workgroup is involved.
 //
-// Tiles move through a three-slot LDS ring (direct global -> LDS loads,
-// 16-byte chunks swizzled by row so the operand reads are conflict free).
+// Keys move through a three-slot LDS ring in steps of 32 keys x 576 columns
+// (direct global -> LDS loads).  One step serves both products: the score
+// reads take 16-byte chunks of each key row, the value reads take the same
+// image through ds_read_b64_tr_b16 transpose reads, so every byte comes into
+// the workgroup once per pass.  Columns 0..511 are stored as four blocks of
+// [32 keys x 128 columns] (256-byte rows), columns 512..575 as a block of
+// [32 keys x 64 columns] (128-byte rows); chunks are XOR-swizzled by row so
+// both read patterns hit distinct banks.
 //
-//  1. Score pass (thresholds > 0 only), 6 steps of 96 columns per tile:
-//     S^T = K Q^T for every tile of the sub-split; each head's tile max goes
-//     to an LDS table.
-//  2. Decision: each half publishes its heads' maxima for later sub-splits of
-//     its chain and folds in those of the earlier ones (the look-back of the
-//     GQA decode), computes its heads' part of every tile's statistic
-//     max_r (tile_max - running_max), and exchanges it with the other half, so
-//     both halves take the same decision for the whole group.
-//  3. Kept tiles, 9 steps of [128 keys x 128 columns] per tile: 5 score steps
-//     (columns 0..511, then the 64 rope columns), p = exp2(s - m) with m the
-//     sub-split's own per-head max (no rescaling), then 4 value steps that
-//     reload columns 0..511 (from L2: the score steps have just read them),
-//     O^T += V^T P^T with V^T from ds_read_b64_tr_b16 transpose reads.
-// With threshold 0 nothing can be skipped: phases 1 and 2 are left out and
-// phase 3 runs over every tile as an online pass (running max, rescale when
-// it grows).
+//  * threshold 0: one online pass (running max, rescale when it has grown by
+//    more than 2^8 -- P stays below 256, exactly representable scaling).
+//  * threshold > 0: a score pass over the sub-split records every head's
+//    tile maxima (LDS table); the decision folds in the maxima of the earlier
+//    sub-splits of the chain (published per head, each read with a launch
+//    tag), so the decisions are those of one streaming pass over the chain;
+//    then the kept tiles are read again, scored, exponentiated against the
+//    sub-split's own per-head max (no rescaling) and multiplied by V.
 //
 // The split's O / l and lse go to the workspace; decode_combine merges splits.
 
@@ -47,31 +50,33 @@
 namespace ssattn {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kDqk = 576;              // latent key width
-constexpr int kDv = 512;               // value width (leading columns of the key row)
-constexpr int kHalf = 64;              // query heads per workgroup
-constexpr int kTmax = 64;              // tiles per sub-split
-constexpr int kSlotBytes = kTile * 256;  // [128 keys x 128 columns] bf16
-constexpr int kQk = kDqk / 32;         // 18 MFMA k-steps over the key width
+constexpr int kDqk = 576;                 // latent key width
+constexpr int kDv = 512;                  // value width (leading columns of the key row)
+constexpr int kHeadsPerWave = 32;
+constexpr int kTmax = 64;                 // tiles per sub-split
+constexpr int kStepKeys = 32;             // keys per ring step
+constexpr int kStepsPerTile = kTile / kStepKeys;
+constexpr int kBlkBytes = kStepKeys * 256;               // [32 keys x 128 columns] bf16
+constexpr int kRopeOff = 4 * kBlkBytes;                  // [32 keys x 64 columns] block
+constexpr int kStepBytes = kRopeOff + kStepKeys * 128;   // 36 KB
+constexpr int kUnits = kStepBytes / 1024;                // 1 KB wave load instructions per step
+constexpr int kQk = kDqk / 16;                           // 36 MFMA k-steps over the key width
+constexpr int kVb = kDv / 32;                            // 16 value-column blocks
+constexpr float kRescaleMargin = 8.f;                    // log2 units (P < 256)
 constexpr int kSpinCap = 1 << 21;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// Physical 16-byte chunk of logical chunk c in row r of a ring step, per
-// step kind, so that each kind's operand reads hit 16 different chunk
-// positions (all banks) per 16 lanes:
-//  * score step, 128 columns (16 chunks, 256-byte rows): 16 consecutive rows
-//    read the same logical chunk -> c ^ (r & 15);
-//  * score step, 64 columns (8 chunks, 128-byte rows, two rows per 256
-//    bytes) -> c ^ ((r >> 1) & 7);
-//  * value step (transpose reads: 4 consecutive rows x 2 adjacent chunks
-//    per 16 lanes) -> c ^ ((r & 7) << 1).
-__device__ __forceinline__ int swz_score128(int r) { return r & 15; }
-__device__ __forceinline__ int swz_score64(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz_value(int r) { return (r & 7) << 1; }
+// Physical 16-byte chunk = logical chunk ^ swizzle(row).
+//  * 256-byte rows (16 chunks): score reads take one chunk of 16 consecutive
+//    rows -> 16 distinct values; value transpose reads take a 32-byte chunk
+//    pair of 4 consecutive rows -> bits 1..2 distinct, pairs kept together.
+//  * 128-byte rows (8 chunks, two rows per 256 bytes): score reads only.
+__device__ __forceinline__ int swz256(int r) {
+  return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+}
+__device__ __forceinline__ int swz128(int r) { return (r >> 1) & 7; }
 
 // s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding).
 template <int N>
@@ -112,6 +117,27 @@ __device__ __forceinline__ float poll_tagged(unsigned long long* p, unsigned tag
   return __uint_as_float((unsigned)v);
 }
 
+// One direct global -> LDS load of 16 bytes per lane: lane l's bytes at
+// gbase + goff land at LDS address lds + 16 l.  Written out rather than through
+// the compiler builtin: with the builtin in a loop the compiler waits for every
+// outstanding LDS read (lgkmcnt 0) before each use of one, which defeats the
+// read-ahead of the MFMA operands.  The ring waits for these loads itself
+// (wait_vmcnt); the compiler's own vmcnt waits count only the loads it knows,
+// which can only make them stricter.  M0 holds the LDS address and is
+// restored; the wait states after each M0 write are the ones the hardware
+// needs before a read of M0.
+__device__ __forceinline__ void dma16(const void* gbase, unsigned goff, const unsigned char* lds) {
+  const unsigned la =
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)lds;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "s"(la), "v"(goff), "s"(gbase)
+      : "memory");
+}
+
 template <class F, int... E>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, E...>) {
   (f(std::integral_constant<int, E>{}), ...);
@@ -122,49 +148,46 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Step plans: the columns each step of a tile brings into the ring.
-struct ScorePlan {  // score pass: all 576 columns
-  static constexpr int P = 6;
-  static constexpr int col[P] = {0, 128, 256, 384, 448, 512};
-  static constexpr int width[P] = {128, 128, 128, 64, 64, 64};
-  static constexpr bool value[P] = {false, false, false, false, false, false};
-};
-struct KeptPlan {  // kept tile: 576 score columns, then the 512 value columns again
-  static constexpr int P = 9;
-  static constexpr int col[P] = {0, 128, 256, 384, 512, 0, 128, 256, 384};
-  static constexpr int width[P] = {128, 128, 128, 128, 64, 128, 128, 128, 128};
-  static constexpr bool value[P] = {false, false, false, false, false, true, true, true, true};
-  static constexpr int kLastScore = 4;
-};
+// The score MFMAs in their VGPR form.  Every builtin MFMA of this kernel is
+// compiled to the accumulation-register form (the [512 x 32] output blocks
+// fill all 256 of them), so the score products, whose results the vector ALU
+// reads, are written out here.  The hardware forwards an accumulator from one
+// MFMA to the next that names it as its own (no wait); the first MFMA of a
+// chain starts from 0 and is preceded by two wait states for a vector ALU
+// write of its operands; mfma_vgpr_drain gives the 24 wait states an MFMA
+// result needs before a vector ALU instruction may read it, and ties the
+// chains so that nothing reads them earlier.
+__device__ __forceinline__ void mfma_vgpr_first(f32x16_t& acc, u32x4_t a, bf16x8_t b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr(f32x16_t& acc, u32x4_t a, bf16x8_t b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_drain(f32x16_t& x, f32x16_t& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
 
-template <int NHALF>
-__global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
-  constexpr int G = NHALF * kHalf;  // heads per latent head
-  __shared__ __attribute__((aligned(1024))) unsigned char slot0[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char slot1[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char slot2[kSlotBytes];
-  __shared__ __attribute__((aligned(16))) float tmaxs[kTmax * kHalf];  // [tile][head]
-  __shared__ float prevred[kWaves][kHalf];
-  __shared__ float s_mref[kHalf];
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
+  constexpr int G = NW * kHeadsPerWave;  // heads per latent head
+  constexpr int kThreads = 64 * NW;
+  constexpr int LPW = kUnits / NW;       // load instructions per wave per step
+  static_assert(LPW * NW == kUnits, "step loads");
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[kStepBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[kStepBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[kStepBytes];
+  __shared__ __attribute__((aligned(16))) float tmaxs[kTmax * G];  // [tile][head]
+  __shared__ float part_red[2][G];
+  __shared__ float s_mref[G];
   __shared__ float s_dtile[kTmax];
   __shared__ int s_surv[kTmax];
   __shared__ int s_nsurv;
+  __shared__ int s_restart;
 
-  // block -> (batch, sub-split, half): sub-splits in order (every look-back
-  // waits only on lower blocks); the two halves of a sub-split are 8 blocks
-  // apart, on the same XCD (blocks go to XCDs round robin), so both read the
-  // same tiles through one L2.
+  // block -> (batch, sub-split): sub-splits in order, so every look-back
+  // waits only on lower blocks (dispatched first)
   const int S = a.num_splits;
-  int half, usub;
-  if (NHALF == 2) {
-    const int grp16 = blockIdx.x >> 4, in16 = blockIdx.x & 15;
-    half = in16 >> 3;
-    usub = grp16 * 8 + (in16 & 7);
-  } else {
-    half = 0;
-    usub = blockIdx.x;
-  }
-  const bool live = usub < S * a.B * a.Hkv;
+  const int usub = blockIdx.x;
   const int sub = usub % S;
   const int pair = usub / S;  // b * Hkv + hk
   const int hk = pair % a.Hkv;
@@ -175,21 +198,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
   const int chain_t0 = chain * a.chain_tiles;
   const int chain_t1 = min(chain_t0 + a.chain_tiles, nK);
   const int t0 = chain_t0 + link * a.tiles_per_split;
-  const int T = live ? max(0, min(t0 + a.tiles_per_split, chain_t1) - t0) : 0;
+  const int T = max(0, min(t0 + a.tiles_per_split, chain_t1) - t0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // wave index as a scalar: everything derived from it (ring destinations,
-  // row bases) stays in scalar registers
+  // wave index as a scalar: everything derived from it stays in scalar registers
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15;
-  const int q = lane >> 4;                   // MFMA k-group of this lane
-  const int head0 = hk * G + half * kHalf;   // first query head of this half
-  const int myhead = w * 16 + l16;           // head within the half owned by this lane
+  const int l32 = lane & 31;
+  const int g = lane >> 5;                    // MFMA k-group of this lane
+  const int head0 = hk * G;                   // first query head of the group
+  const int myhead = w * kHeadsPerWave + l32;  // head within the group owned by this lane
 
-  if (!live) return;  // padding block of the half-interleaved grid
-  if (T == 0) {       // an empty trailing link: nothing to publish, nobody waits on it
-    for (int idx = tid; idx < kHalf * kDv; idx += kThreads) {
+  if (T == 0) {  // an empty trailing link: nothing to publish, nobody waits on it
+    for (int idx = tid; idx < G * kDv; idx += kThreads) {
       const size_t rowid = ((size_t)sub * a.B + b) * a.Hq + head0 + idx / kDv;
       a.part_o[rowid * kDv + idx % kDv] = 0.f;
       if (idx % kDv == 0) a.part_lse[rowid] = neg_inf();
@@ -197,28 +218,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
     return;
   }
 
-  const unsigned short* kp =
-      static_cast<const unsigned short*>(a.k) + ((size_t)pair * a.Lk) * kDqk;
+  const unsigned char* kp = static_cast<const unsigned char*>(a.k) + (size_t)pair * a.Lk * (kDqk * 2);
   const float c = a.scale * kLog2e;
   const bool dense = a.log2_thr == neg_inf();
 
-  // Q^T operands: lane holds head myhead, dims 32 j + 8 q .. + 8 for j < 18
+  // Q^T operands: lane holds head myhead, dims [16 ks + 8 g, +8) for ks < 36
   bf16x8_t qf[kQk];
   {
     const unsigned short* qp =
         static_cast<const unsigned short*>(a.q) + ((size_t)b * a.Hq + head0 + myhead) * kDqk;
 #pragma unroll
-    for (int j = 0; j < kQk; ++j)
-      qf[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + j * 32 + q * 8));
-    // keep these loads ahead of the ring's first loads, so waiting for Q
-    // does not wait for the ring
-    asm volatile("" ::: "memory");
+    for (int ks = 0; ks < kQk; ++ks)
+      qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + ks * 16 + g * 8));
+    // Q has landed before the ring starts: the compiler's waits for these
+    // loads would otherwise also count (and wait for) the ring's loads
+    wait_vmcnt<0>();
   }
 
-  // ---- the ring: three LDS slots.  A tile is a fixed number of steps (6 in
-  // the score pass, 9 for a kept tile), a multiple of three, so step e of
-  // every tile uses slot e % 3: the slot and the step kind are compile-time
-  // constants, and so is every register-array index below.
   auto slot = [&](auto I) __attribute__((always_inline)) -> unsigned char* {
     constexpr int i = decltype(I)::value % 3;
     if constexpr (i == 0) return slot0;
@@ -226,309 +242,359 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(DecodeArgs a) {
     else return slot2;
   };
 
-  // A step holds W = 128 or 64 columns from column C of the tile's 128 keys:
-  // rows of 2 W bytes, 16-byte chunks swizzled by the step kind's rule above.
-  // Wave w loads rows [32 w, 32 w + 32), 1024 bytes per instruction.  Keys
-  // past Lk read the last key row (their scores are masked, their p is 0).
-  auto issue = [&](auto C_, auto W_, auto V_, int tile, unsigned char* dst)
-                   __attribute__((always_inline)) {
-    constexpr int C = decltype(C_)::value, W = decltype(W_)::value;
-    constexpr bool V = decltype(V_)::value;
-    constexpr int CPR = W / 8;         // chunks per row
-    constexpr int RPI = 64 / CPR;      // rows per instruction
-    constexpr int NI = 32 / RPI;       // instructions per wave
-    const int lr = lane / CPR, pc = lane % CPR;
+  auto issue = [&](int tile, int st, unsigned char* dst) __attribute__((always_inline)) {
+    // a step that starts past Lk (tail tile) reads the last key row throughout
+    const int key0 = min(tile * kTile + st * kStepKeys, a.Lk - 1);
+    const int rlast = a.Lk - 1 - key0;  // last valid row of this step (>= 0)
+    const unsigned char* src = kp + (size_t)key0 * (kDqk * 2);
+    const int ln = lane_id_fresh();
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = (w * NI + i) * RPI + lr;
-      const int key = min(tile * kTile + r, a.Lk - 1);
-      const int lc = pc ^ (V ? swz_value(r) : (W == 128 ? swz_score128(r) : swz_score64(r)));
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(kp + (size_t)key * kDqk + C + lc * 8),
-          (void __attribute__((address_space(3)))*)(dst + (w * NI + i) * 1024), 16, 0, 0);
+    for (int i = 0; i < LPW; ++i) {
+      const int ui = i * NW;  // compile-time part of the unit
+      int row, col_byte, dst_off;
+      if (ui < 32) {
+        const int cb = ui / 8;
+        row = 4 * (ui % 8 + w) + (ln >> 4);
+        const int lc = (ln & 15) ^ swz256(row);
+        col_byte = cb * 256 + lc * 16;
+        dst_off = cb * kBlkBytes + (ui % 8 + w) * 1024;
+      } else {
+        const int up = ui - 32 + w;
+        row = 8 * up + (ln >> 3);
+        const int lc = (ln & 7) ^ swz128(row);
+        col_byte = 1024 + lc * 16;
+        dst_off = kRopeOff + up * 1024;
+      }
+      const unsigned ro = (unsigned)min(row, rlast) * (kDqk * 2) + col_byte;
+      dma16(src, ro, dst + dst_off);
     }
   };
 
-  // S^T blocks [16 keys x 16 heads], block kb = keys 16 kb .. of the tile;
-  // lane holds head l16, keys 16 kb + 4 q + i
-  f32x4_t sacc[8];
-  // scores over the step's columns: k-step ks (32 columns) reads logical
-  // chunk 4 ks + q of row 16 kb + l16
-  auto score = [&](auto C_, auto W_, const unsigned char* sl) __attribute__((always_inline)) {
-    constexpr int C = decltype(C_)::value, W = decltype(W_)::value;
-    constexpr int NKS = W / 32;
-    if constexpr (C == 0) {
+  // Per-lane LDS offsets of the score operand reads (row l32; k-step ks reads
+  // logical chunk 2 (ks % 8) + g of block ks / 8, or chunk 2 (ks - 32) + g of
+  // the 128-byte block): the block is an immediate offset.
+  int koff[8], koff4[4];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k8 = 0; k8 < 8; ++k8) koff[k8] = l32 * 256 + (((2 * k8 + g) ^ swz256(l32)) << 4);
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4)
+    koff4[k4] = kRopeOff + l32 * 128 + (((2 * k4 + g) ^ swz128(l32)) << 4);
+  // ... of the value transpose reads.  Value block vb (columns 32 vb ..),
+  // 16-key k-step t, half hi: lane l reads row 16 t + 8 hi + 4 g + (l & 15) / 4,
+  // 8 bytes at column 32 vb + 16 ((l >> 4) & 1) + 4 (l & 3).  The swizzle of
+  // that row does not depend on t, and on vb only through an XOR of bits 2..3
+  // of the chunk, so 8 offsets (hi, vb % 4) cover every read.
+  int voff[2][4];
+  {
+    const int r16 = lane & 15;
+    const int x = 2 * ((lane >> 4) & 1) + ((r16 & 3) >> 1);  // chunk bits 0..1
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = 8 * hi + 4 * g + (r16 >> 2);
+      const int sw = swz256(row);
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        voff[hi][v4] = row * 256 + (((4 * v4 + x) ^ sw) << 4) + (r16 & 1) * 8;
     }
-    // rows 16 kb + l16: the swizzle depends on l16 only, the row block is an
-    // immediate offset
-    const int sw = W == 128 ? swz_score128(l16) : swz_score64(l16);
-    const unsigned char* base = sl + l16 * (2 * W);
-    auto read = [&](int ks, u32x4_t (&kv)[8]) __attribute__((always_inline)) {
-      const int off = ((4 * ks + q) ^ sw) << 4;
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-        kv[kb] = *reinterpret_cast<const u32x4_t*>(base + kb * 16 * (2 * W) + off);
+  }
+
+  // S^T = K Q^T over one step, two accumulation chains (even and odd
+  // k-steps) so that consecutive MFMAs are independent.  Operand reads run
+  // kPre k-steps ahead of their MFMA; the scheduling barriers keep that order.
+  // Lane l ends up with head l32, keys 8 j + 4 g + r in element 4 j + r.
+  auto scores = [&](const unsigned char* sl) __attribute__((always_inline)) -> f32x16_t {
+    constexpr int kPre = 4;
+    auto read = [&](int ks) __attribute__((always_inline)) {
+      const int off = ks < 32 ? (ks / 8) * kBlkBytes + koff[ks % 8] : koff4[ks - 32];
+      return *reinterpret_cast<const u32x4_t*>(sl + off);
     };
-    // operands of k-step ks + 1 are read while the MFMAs of k-step ks run
-    u32x4_t kv[2][8];
-    read(0, kv[0]);
+    u32x4_t kv[kPre];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (ks + 1 < NKS) read(ks + 1, kv[(ks + 1) & 1]);
+    for (int p = 0; p < kPre; ++p) kv[p] = read(p);
+    f32x16_t acc[2];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks & 1][kb]),
-                                                          qf[C / 32 + ks], sacc[kb], 0, 0, 0);
+    for (int ks = 0; ks < kQk; ++ks) {
+      const u32x4_t cur = kv[ks % kPre];
+      if (ks + kPre < kQk) kv[ks % kPre] = read(ks + kPre);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks < 2)
+        mfma_vgpr_first(acc[ks & 1], cur, qf[ks]);
+      else
+        mfma_vgpr(acc[ks & 1], cur, qf[ks]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // schedule: the first k-step's reads, then one MFMA per read of the next
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    mfma_vgpr_drain(acc[0], acc[1]);
 #pragma unroll
-    for (int i = 0; i < 8 * (NKS - 1); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    for (int i = 0; i < 16; ++i) acc[0][i] += acc[1][i];
+    return acc[0];
   };
 
-  // scores of the tile in log2 units, keys past Lk at -inf; returns the tile
-  // max of head myhead (every lane of the head agrees)
-  auto finish_scores = [&](int tile) __attribute__((always_inline)) {
-    const int kbase = tile * kTile + q * 4;
+  // raw scores of keys past Lk -> -inf (only the tail step of a sequence)
+  auto mask_tail = [&](f32x16_t& s, int key0) __attribute__((always_inline)) {
+    if (key0 + kStepKeys > a.Lk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + 8 * (i >> 2) + 4 * g + (i & 3) >= a.Lk) s[i] = neg_inf();
+    }
+  };
+
+  // the head's max over the step in log2 units (c > 0 keeps the order)
+  auto head_max = [&](const f32x16_t& s) __attribute__((always_inline)) {
     float m = neg_inf();
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float s = sacc[kb][i] * c;
-        if (kbase + kb * 16 + i >= a.Lk) s = neg_inf();
-        sacc[kb][i] = s;
-        m = fmaxf(m, s);
-      }
-    m = fmaxf(m, shfl_xor_f(m, 16));
-    return fmaxf(m, shfl_xor_f(m, 32));
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, s[i]);
+    return max_xor32(m) * c;  // lanes l and l ^ 32 hold the same head
   };
 
-  // Run `nt` tiles through the ring, PLAN::P steps each.  Every step issues the
-  // loads of the step two ahead; past the last tile it repeats the same step
-  // kind of the last tile, so the loads in flight at every wait are known:
-  // this step's and the next step's.
-  auto pipeline = [&](int nt, auto plan, auto&& tile_of, auto&& body) __attribute__((always_inline)) {
-    using PL = decltype(plan);
-    constexpr int P = PL::P;
-    static_assert(P % 3 == 0, "steps per tile");
-    auto load = [&](int t, auto E, unsigned char* dst) __attribute__((always_inline)) {
-      constexpr int e = decltype(E)::value;
-      issue(std::integral_constant<int, PL::col[e]>{}, std::integral_constant<int, PL::width[e]>{},
-            std::integral_constant<bool, PL::value[e]>{}, tile_of(min(t, nt - 1)), dst);
+  // O^T accumulators: block vb holds value columns 32 vb + 8 j + 4 g + r of head l32
+  f32x16_t oacc[kVb];
+#pragma unroll
+  for (int vb = 0; vb < kVb; ++vb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[vb][i] = 0.f;
+  float lpart = 0.f;  // this lane's share of the head's denominator
+
+  // p = exp2(s c - mref) from raw scores s, lpart += p, then O^T += V^T P^T
+  // over the step's keys
+  auto accumulate = [&](const f32x16_t& s, float mref, const unsigned char* sl)
+                        __attribute__((always_inline)) {
+    // O^T += V^T P^T: 32 MFMAs (k-step t, value block vb); the two transpose
+    // reads of each run kPre MFMAs ahead, the first ones under the exponentials
+    constexpr int kPre = 4;
+    auto read = [&](int n) __attribute__((always_inline)) {
+      const int t = n / kVb, vb = n % kVb;
+      const unsigned char* base = sl + (vb / 4) * kBlkBytes + t * 16 * 256;
+      const s16x4_t lo =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + voff[0][vb % 4]));
+      const s16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + voff[1][vb % 4]));
+      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+      const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+      return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
     };
-    load(0, std::integral_constant<int, 0>{}, slot0);
-    load(0, std::integral_constant<int, 1>{}, slot1);
-    for (int t = 0; t < nt; ++t) {
-      const int tile = tile_of(t);
-      static_for<P>([&](auto E) __attribute__((always_inline)) {
-        constexpr int e = decltype(E)::value;
-        constexpr int en = (e + 1) % P;
-        wait_vmcnt<PL::width[en] / 16>();  // this step's loads have landed, the next one's may not
-        lds_barrier();  // everyone's have, and everyone is done with the previous step
-        constexpr int e2 = e + 2;
-        if constexpr (e2 < P)
-          load(t, std::integral_constant<int, e2>{}, slot(std::integral_constant<int, e2>{}));
-        else
-          load(t + 1, std::integral_constant<int, e2 - P>{}, slot(std::integral_constant<int, e2>{}));
-        body(E, std::integral_constant<int, PL::col[e]>{},
-             std::integral_constant<int, PL::width[e]>{}, tile, slot(E));
+    u32x4_t vv[kPre];
+#pragma unroll
+    for (int p = 0; p < kPre; ++p) vv[p] = read(p);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      unsigned pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(fmaf(s[8 * t + 2 * e], c, -mref));
+        const float p1 = fast_exp2(fmaf(s[8 * t + 2 * e + 1], c, -mref));
+        lpart += p0 + p1;
+        pw[e] = pack_bf16x2(p0, p1);
+      }
+      pb[t] = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+    }
+#pragma unroll
+    for (int n = 0; n < 2 * kVb; ++n) {
+      const u32x4_t cur = vv[n % kPre];
+      if (n + kPre < 2 * kVb) vv[n % kPre] = read(n + kPre);
+      __builtin_amdgcn_sched_barrier(0);
+      oacc[n % kVb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), pb[n / kVb],
+                                                             oacc[n % kVb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Run `nsteps` ring steps; step e covers keys 32 (e % 4) .. of tile
+  // tile_of(e / 4).  Every step issues the loads of the step two ahead (past
+  // the end: the last step again); the loop is unrolled by three so every
+  // step names its slot at compile time.  The waits, barriers and loads of
+  // the three steps run unconditionally (steps past the end, up to the next
+  // multiple of three, load and compute nothing new), so the loads in flight
+  // at every wait are the same on every path: this step's and the next one's.
+  // stop() is read after each step's barrier (so it may read LDS written in
+  // the step before) and ends the pass early, uniformly over the workgroup.
+  auto pipeline = [&](int nsteps, auto&& tile_of, auto&& body, auto&& stop)
+                      __attribute__((always_inline)) {
+    auto load = [&](int e, unsigned char* dst) __attribute__((always_inline)) {
+      const int ec = min(e, nsteps - 1);
+      issue(tile_of(ec >> 2), ec & 3, dst);
+    };
+    load(0, slot0);
+    load(1, slot1);
+    bool done = false;
+    for (int e0 = 0; e0 < nsteps && !done; e0 += 3) {
+      static_for<3>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        const int e = e0 + i;
+        wait_vmcnt<LPW>();  // this step's loads have landed, the next one's may not
+        lds_barrier();      // everyone's have, and everyone is done with step e - 1
+        if (!done && stop()) done = true;
+        load(e + 2, slot(std::integral_constant<int, i + 2>{}));
+        if (!done && e < nsteps) body(slot(I), tile_of(e >> 2), e & 3);
       });
     }
     wait_vmcnt<0>();
     __syncthreads();
   };
+  auto never = []() __attribute__((always_inline)) { return false; };
 
-  // ------------------------------------------------------------ 1. score pass
-  if (!dense) {
-    pipeline(T, ScorePlan{}, [&](int t) __attribute__((always_inline)) { return t0 + t; },
-             [&](auto E, auto C_, auto W_, int tile, const unsigned char* sl)
-                 __attribute__((always_inline)) {
-               score(C_, W_, sl);
-               if constexpr (decltype(E)::value == ScorePlan::P - 1) {
-                 const float m = finish_scores(tile);
-                 if (q == 0) tmaxs[(tile - t0) * kHalf + myhead] = m;
-               }
-             });
-  }
-
-  // ------------------------------------------------------------ 2. decision
   const unsigned tag = a.lb_tag;
   const size_t lbslot = (size_t)pair * S + sub;
+  float mref = neg_inf();  // exponent reference of head myhead (log2 units)
+  int nkept = T;
+
   if (!dense) {
-    // the sub-split's own per-head max
-    const int h = tid & 63;
+    // ---------------------------------------------------------- 1. score pass
+    float tmax = neg_inf();
+    pipeline(kStepsPerTile * T, [&](int t) __attribute__((always_inline)) { return t0 + t; },
+             [&](const unsigned char* sl, int tile, int st) __attribute__((always_inline)) {
+               f32x16_t s = scores(sl);
+               mask_tail(s, tile * kTile + st * kStepKeys);
+               tmax = fmaxf(tmax, head_max(s));
+               if (st == kStepsPerTile - 1) {
+                 if (g == 0) tmaxs[(tile - t0) * G + myhead] = tmax;
+                 tmax = neg_inf();
+               }
+             },
+             never);
+
+    // ---------------------------------------------------------- 2. decision
+    // thread (part, h): head h, tiles / earlier links of parity `part`
+    const int h = tid % G, part = tid / G;  // part in {0, 1}
     float cm = neg_inf();
-    for (int t = tid >> 6; t < T; t += kWaves) cm = fmaxf(cm, tmaxs[t * kHalf + h]);
-    prevred[w][h] = cm;
+    for (int t = part; t < T; t += 2) cm = fmaxf(cm, tmaxs[t * G + h]);
+    part_red[part][h] = cm;
     __syncthreads();
-    if (w == 0) {
-      cm = fmaxf(fmaxf(prevred[0][h], prevred[1][h]), fmaxf(prevred[2][h], prevred[3][h]));
+    cm = fmaxf(part_red[0][h], part_red[1][h]);
+    if (part == 0) {
       s_mref[h] = cm;
       if (a.subs_per_chain > 1)
-        __hip_atomic_store(&a.lb_slot[lbslot * G + half * kHalf + h], tagged(tag, cm),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.lb_slot[lbslot * G + h], tagged(tag, cm), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
-    // earlier links of the chain: every thread polls some (link, head) pairs
+    // earlier links of the chain: eight reads in flight at a time (by then
+    // the earlier links have usually published), a poll only for a value
+    // not yet published
     float pv = neg_inf();
-    for (int lk = tid >> 6; lk < link; lk += kWaves) {
-      const size_t ps = (size_t)pair * S + (sub - link) + lk;
-      pv = fmaxf(pv, poll_tagged(&a.lb_slot[ps * G + half * kHalf + h], tag, a.lb_timeouts));
+    const size_t chain_slot0 = (size_t)pair * S + (sub - link);
+    for (int lk0 = part; lk0 < link; lk0 += 16) {
+      unsigned long long v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int lk = lk0 + 2 * j;
+        v[j] = lk < link ? __hip_atomic_load(&a.lb_slot[(chain_slot0 + lk) * G + h],
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : tagged(tag, neg_inf());
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int lk = lk0 + 2 * j;
+        const float x = (v[j] >> 32) == tag
+                            ? __uint_as_float((unsigned)v[j])
+                            : poll_tagged(&a.lb_slot[(chain_slot0 + lk) * G + h], tag,
+                                          a.lb_timeouts);
+        pv = fmaxf(pv, x);
+      }
     }
-    __syncthreads();  // the reads of prevred above are done
-    prevred[w][h] = pv;
+    __syncthreads();  // part_red reads above are done
+    part_red[part][h] = pv;
     __syncthreads();
-    // every wave scans all tiles for head h and reduces over heads for the
-    // tiles t = w (mod 4)
-    {
-      float M = fmaxf(fmaxf(prevred[0][h], prevred[1][h]), fmaxf(prevred[2][h], prevred[3][h]));
+    if (part == 0) {
+      // running max before each tile, and each tile's statistic for head h
+      // (written over its tile max)
+      float M = fmaxf(part_red[0][h], part_red[1][h]);
       for (int t = 0; t < T; ++t) {
-        const float tm = tmaxs[t * kHalf + h];
+        const float tm = tmaxs[t * G + h];
         float d = neg_inf();
         if (tm != neg_inf()) d = (M == neg_inf()) ? pos_inf() : tm - M;
-        if ((t & 3) == w) {
-          d = wave_max(d);
-          if (lane == 0) s_dtile[t] = d;
-        }
+        tmaxs[t * G + h] = d;
         M = fmaxf(M, tm);
       }
     }
     __syncthreads();
+    // max over heads per tile: wave w reduces the tiles t = w (mod NW)
+    for (int t = w; t < T; t += NW) {
+      float d = neg_inf();
+#pragma unroll
+      for (int j = 0; j < G / 64; ++j) d = fmaxf(d, tmaxs[t * G + j * 64 + lane]);
+      d = wave_max(d);
+      if (lane == 0) s_dtile[t] = d;
+    }
+    __syncthreads();
     if (w == 0) {
       const bool valid = lane < T;
-      float d = valid ? s_dtile[lane] : neg_inf();
-      if (NHALF == 2) {  // the other half's heads
-        const size_t xs = (lbslot * 2 + half) * kTmax + lane;
-        const size_t xo = (lbslot * 2 + (half ^ 1)) * kTmax + lane;
-        if (valid) {
-          __hip_atomic_store(&a.lb_xchg[xs], tagged(tag, d), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-          d = fmaxf(d, poll_tagged(&a.lb_xchg[xo], tag, a.lb_timeouts));
-        }
-      }
+      const float d = valid ? s_dtile[lane] : neg_inf();
       const bool kept = valid && !(d < a.log2_thr);
       const unsigned long long bits = __ballot(kept);
       const int idx = __popcll(bits & ((1ull << lane) - 1ull));
       if (kept) s_surv[idx] = lane;
       if (lane == 0) s_nsurv = __popcll(bits);
-      if (valid && half == 0 && a.mask) a.mask[(size_t)pair * nK + t0 + lane] = kept ? 0 : 1;
+      if (valid && a.mask) a.mask[(size_t)pair * nK + t0 + lane] = kept ? 0 : 1;
     }
     __syncthreads();
+    nkept = s_nsurv;
+    mref = s_mref[myhead];
+
+    // ---------------------------------------------------------- 3. kept tiles
+    if (nkept > 0) {
+      const float mr = mref == neg_inf() ? 0.f : mref;
+      pipeline(kStepsPerTile * nkept,
+               [&](int t) __attribute__((always_inline)) { return t0 + s_surv[t]; },
+               [&](const unsigned char* sl, int tile, int st) __attribute__((always_inline)) {
+                 f32x16_t s = scores(sl);
+                 mask_tail(s, tile * kTile + st * kStepKeys);
+                 accumulate(s, mr, sl);
+               },
+               never);
+    }
   } else {
-    if (half == 0 && a.mask)
+    // ---------------------------------------------------------- online pass
+    // The exponent reference of each head is its max over the first step;
+    // p = exp2(s - mref) may reach 2^8 (exact in fp32 and bf16 alike).  When
+    // some head's scores rise further above it, the pass starts over with
+    // every head's running max as its reference (rewriting the accumulators
+    // in place would cost a copy of all 256 of them through the vector ALU
+    // at every step; starting over happens only for score ranges above 2^8).
+    if (a.mask)
       for (int t = tid; t < T; t += kThreads) a.mask[(size_t)pair * nK + t0 + t] = 0;
+    float mrun = neg_inf();  // running max of head myhead over the steps seen
+    for (;;) {
+#pragma unroll
+      for (int vb = 0; vb < kVb; ++vb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[vb][i] = 0.f;
+      lpart = 0.f;
+      if (tid == 0) s_restart = 0;
+      __syncthreads();
+      pipeline(kStepsPerTile * T, [&](int t) __attribute__((always_inline)) { return t0 + t; },
+               [&](const unsigned char* sl, int tile, int st) __attribute__((always_inline)) {
+                 f32x16_t s = scores(sl);
+                 mask_tail(s, tile * kTile + st * kStepKeys);
+                 const float sm = head_max(s);
+                 mrun = fmaxf(mrun, sm);
+                 if (mref == neg_inf()) mref = sm;  // first step (always has a valid key)
+                 if (__builtin_amdgcn_ballot_w64(sm > mref + kRescaleMargin) != 0) {
+                   if (lane == 0) s_restart = 1;
+                 } else {
+                   accumulate(s, mref, sl);
+                 }
+               },
+               [&]() __attribute__((always_inline)) { return s_restart != 0; });
+      if (s_restart == 0) break;
+      mref = mrun;
+      __syncthreads();  // everyone has read s_restart
+    }
   }
 
-  // ------------------------------------------------------------ 3. kept tiles
-  f32x4_t oacc[32];  // O^T blocks [16 value columns x 16 heads]: columns 16 i + 4 q + j
-#pragma unroll
-  for (int i = 0; i < 32; ++i) oacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrun = dense ? neg_inf() : s_mref[myhead];
-  float lpart = 0.f;  // this lane's keys of the kept tiles
-  unsigned int pw[4][4];  // P of the tile as the P.V B operand, per 32-key step
-  const int nkept = dense ? T : s_nsurv;
-
-  auto kept_step = [&](auto E, auto C_, auto W_, int tile, const unsigned char* sl)
-                       __attribute__((always_inline)) {
-    constexpr int e = decltype(E)::value;
-    constexpr int C = decltype(C_)::value;
-    if constexpr (!KeptPlan::value[e]) {
-      score(C_, W_, sl);
-      if constexpr (e == KeptPlan::kLastScore) {
-        const float m = finish_scores(tile);
-        if (dense) {  // online pass
-          const float mnew = fmaxf(mrun, m);
-          if (__builtin_amdgcn_ballot_w64(mnew != mrun) != 0) {
-            const float alpha = fast_exp2(mrun - (mnew == neg_inf() ? 0.f : mnew));
-            lpart *= alpha;
-#pragma unroll
-            for (int i = 0; i < 32; ++i)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) oacc[i][j] *= alpha;
-          }
-          mrun = mnew;
-        }
-        const float mref = mrun == neg_inf() ? 0.f : mrun;
-        // 32-key step j takes blocks 2 j and 2 j + 1: k-elements 0..3 are the
-        // lane's keys of the first, 4..7 those of the second
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const float p0 = fast_exp2(sacc[2 * j + hb][0] - mref);
-            const float p1 = fast_exp2(sacc[2 * j + hb][1] - mref);
-            const float p2 = fast_exp2(sacc[2 * j + hb][2] - mref);
-            const float p3 = fast_exp2(sacc[2 * j + hb][3] - mref);
-            lpart += (p0 + p1) + (p2 + p3);
-            pw[j][hb * 2] = pack_bf16x2(p0, p1);
-            pw[j][hb * 2 + 1] = pack_bf16x2(p2, p3);
-          }
-      }
-    } else {
-      // value columns C + 16 cb + l16 for cb < 8.  The A operand V^T of
-      // 32-key step j: rows 32 j + 4 q + (l16 >> 2) and + 16 (the keys of P's
-      // k-elements), 4 columns from 4 (l16 & 3) of the block.
-      const int rr = q * 4 + (l16 >> 2);  // row within the 16-key block
-      const int sw = swz_value(rr);       // rows 32 j + rr and + 16 share it
-      const int cq = (l16 & 3) * 4;       // first of the lane's 4 columns
-      const unsigned char* base = sl + rr * 256 + (cq & 7) * 2;
-      auto read = [&](int j, u32x4_t (&vv)[8]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          const int off = ((2 * cb + (cq >> 3)) ^ sw) << 4;
-          const s16x4_t lo =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + 32 * j * 256 + off));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(base + (32 * j + 16) * 256 + off));
-          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
-          const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
-          vv[cb] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
-        }
-      };
-      // V^T operands of 32-key step j + 1 are read while the MFMAs of step j run
-      u32x4_t vv[2][8];
-      read(0, vv[0]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j + 1 < 4) read(j + 1, vv[(j + 1) & 1]);
-        const bf16x8_t pb = as_bf16x8(u32x4_t{pw[j][0], pw[j][1], pw[j][2], pw[j][3]});
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          constexpr int ob = C / 16;
-          oacc[ob + cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv[j & 1][cb]), pb,
-                                                                 oacc[ob + cb], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-      for (int i = 0; i < 24; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    }
-  };
-  if (nkept > 0)
-    pipeline(nkept, KeptPlan{},
-             [&](int t) __attribute__((always_inline)) { return dense ? t0 + t : t0 + s_surv[t]; },
-             kept_step);
-
   // ------------------------------------------------------------ write O / l and lse
-  const float l = lpart + shfl_xor_f(lpart, 16) + shfl_xor_f(lpart + shfl_xor_f(lpart, 16), 32);
+  const float l = sum_xor32(lpart);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const size_t rowid = ((size_t)sub * a.B + b) * a.Hq + head0 + myhead;
   float* op = a.part_o + rowid * kDv;
 #pragma unroll
-  for (int i = 0; i < 32; ++i)
-    *reinterpret_cast<f32x4_t*>(op + i * 16 + q * 4) =
-        f32x4_t{oacc[i][0] * inv, oacc[i][1] * inv, oacc[i][2] * inv, oacc[i][3] * inv};
-  if (q == 0) a.part_lse[rowid] = l > 0.f ? (mrun + __log2f(l)) * kLn2 : neg_inf();
+  for (int vb = 0; vb < kVb; ++vb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<f32x4_t*>(op + vb * 32 + j * 8 + g * 4) =
+          f32x4_t{oacc[vb][4 * j] * inv, oacc[vb][4 * j + 1] * inv, oacc[vb][4 * j + 2] * inv,
+                  oacc[vb][4 * j + 3] * inv};
+  if (g == 0) a.part_lse[rowid] = l > 0.f ? (mref + __log2f(l)) * kLn2 : neg_inf();
 }
 
 }  // namespace
@@ -539,20 +605,17 @@ bool decode_mla_supported(int D, int Dv, int group, bool latent) {
 
 int decode_mla_max_tiles(int) { return kTmax; }
 
-int decode_mla_workgroups_per_split(int group) { return group / kHalf; }
+int decode_mla_workgroups_per_split(int) { return 1; }
 
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const size_t units = (size_t)a.num_splits * a.B * a.Hkv;
-  if (G == 128) {
-    // halves interleaved in groups of 16 blocks: pad to a multiple of 8 sub-splits
-    const size_t blocks = (units + 7) / 8 * 16;
-    hipLaunchKernelGGL((decode_mla_kernel<2>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-  } else if (G == 64) {
-    hipLaunchKernelGGL((decode_mla_kernel<1>), dim3((unsigned)units), dim3(kThreads), 0, s, a);
-  } else {
+  const dim3 grid((unsigned)((size_t)a.num_splits * a.B * a.Hkv));
+  if (G == 128)
+    hipLaunchKernelGGL((decode_mla_kernel<4>), grid, dim3(256), 0, s, a);
+  else if (G == 64)
+    hipLaunchKernelGGL((decode_mla_kernel<2>), grid, dim3(128), 0, s, a);
+  else
     return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

@@ -49,8 +49,6 @@ struct DecodeArgs {
   // earlier sub-splits of its chain before deciding.
   unsigned lb_tag;                 // nonzero, unique per launch (wraps after 2^31)
   unsigned long long* lb_slot;     // [S][B][Hkv][G] (tag << 32) | float bits
-  unsigned long long* lb_xchg;     // latent decode: [S][B][Hkv][2][64] per-tile statistic
-                                   // of each half of the head group (null otherwise)
   unsigned int* lb_timeouts;       // count of look-back waits that gave up
   // Paged caches (GQA decode): k, v point at [num_blocks, Hkv, 2^block_log2, D]
   // caches, sequence b has seq_lens[b] keys (Lk is their upper bound) whose

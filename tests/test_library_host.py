@@ -138,7 +138,7 @@ def test_split_policy_is_deterministic_and_bounded(ss):
         assert 1 <= s <= nK
     assert ss.ss_decode_num_splits(1, 3, 2, 100, 128, 128) == 0  # Hq % Hkv
     # latent decode (576-wide rows, 512 value columns, one latent head): a
-    # sub-split runs as one workgroup per 64 query heads, 512 workgroups
+    # sub-split runs as one workgroup for all query heads, 256 workgroups
     # wanted, at most 64 tiles per sub-split
     assert ss.ss_decode_num_splits(8, 128, 1, 16384, 576, 512) == 32   # 4 tiles each
     assert ss.ss_decode_num_splits(8, 128, 1, 131072, 576, 512) == 32  # 32 tiles each
@@ -163,14 +163,12 @@ def test_workspace_bytes(ss):
     assert n >= 3 * 4 * 128 * 4
     for args in [(16, 32, 8, 32768, 128, 128, 0), (2, 8, 2, 1000, 64, 64, 99)]:
         assert ss.ss_attn_decode_workspace_bytes(*args) > 0
-    # latent decode: split outputs, lse, per-row maxima, then the two halves'
-    # per-tile exchange ([sub-splits][B][2][64] 64-bit values)
+    # latent decode: split outputs, lse, per-row maxima
     S = 32  # B8 Hq128 Lk16384: 32 sub-splits of 4 tiles
     o = S * 8 * 128 * 512 * 4
     lse = S * 8 * 128 * 4
     slots = S * 8 * 128 * 8
-    xchg = S * 8 * 2 * 64 * 8
-    assert ss.ss_attn_decode_workspace_bytes(8, 128, 1, 16384, 576, 512, 0) == o + lse + slots + xchg + 256
+    assert ss.ss_attn_decode_workspace_bytes(8, 128, 1, 16384, 576, 512, 0) == o + lse + slots + 256
 
 
 # --------------------------------------------------------------------------- argument checks
