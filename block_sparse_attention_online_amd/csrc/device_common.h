@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace ssattn {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -130,6 +133,57 @@ __device__ __forceinline__ float lanes_sum_from(float x) {
 #pragma unroll
   for (int m = 32; m >= LO; m >>= 1) x += shfl_xor_f(x, m);
   return x;
+}
+
+
+// ---- direct-to-LDS rings ------------------------------------------------------
+
+// s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the ring.  __syncthreads (and any release fence that
+// covers LDS) waits for every outstanding direct-to-LDS load, which would
+// leave one step in flight instead of two; this barrier waits only for the
+// wave's own LDS operations (lgkmcnt), and the "memory" clobber keeps the
+// compiler from moving memory accesses across it.  Direct-to-LDS loads are
+// waited for explicitly (wait_vmcnt) before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One direct global -> LDS load of 16 bytes per lane: lane l's bytes at
+// gbase + goff land at LDS address lds + 16 l.  Written out rather than through
+// the compiler builtin: with the builtin in a loop the compiler waits for every
+// outstanding LDS read (lgkmcnt 0) before each use of one, which defeats the
+// read-ahead of the MFMA operands.  The ring waits for these loads itself
+// (wait_vmcnt); the compiler's own vmcnt waits count only the loads it knows,
+// which can only make them stricter.  M0 holds the LDS address and is
+// restored; the wait states after each M0 write are the ones the hardware
+// needs before a read of M0.
+__device__ __forceinline__ void dma16(const void* gbase, unsigned goff, const unsigned char* lds) {
+  const unsigned la =
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)lds;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "s"(la), "v"(goff), "s"(gbase)
+      : "memory");
+}
+
+template <class F, int... E>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, E...>) {
+  (f(std::integral_constant<int, E>{}), ...);
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>)
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // ---- key-tile visit order ---------------------------------------------------------

@@ -51,9 +51,17 @@ constexpr int kRowWaves = 4;  // waves per head: 4 x 32 rows
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// Physical 16-byte chunk of logical chunk c in row r of the K image
-// (A-operand reads: 8 lanes on 8 consecutive rows, same logical chunk).
-__device__ __forceinline__ int k_slot(int r, int c) { return c ^ (r & 7); }
+// Physical 16-byte chunk of logical chunk c in row r of the K image.  The
+// A-operand reads take the same logical chunk of 16 consecutive rows in one
+// LDS cycle (16 lanes x 16 bytes over 64 four-byte banks), so those 16 chunks
+// must sit in 16 different 16-byte bank groups: with 256-byte rows (D = 128)
+// every row starts at bank 0 and the chunk is XORed with four row bits; with
+// 128-byte rows (D = 64) two rows share a bank line and the chunk is XORed
+// with the pair index.
+template <int D>
+__device__ __forceinline__ int k_slot(int r, int c) {
+  return D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+}
 // ... of the V image (transpose reads: 4 consecutive rows x 32 bytes).
 __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r & 3) << 1); }
 
@@ -119,11 +127,13 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   if (mask_writer && plan.causal)
     for (int j = plan.last + 1 + lane; j < nK; j += 64) mrow[j] = 2;
   // per-row decisions: this lane's row of the row mask (lane half 0 writes)
-  uint8_t* const rrow = (a.row_mask && g == 0 && row_ok)
-                            ? a.row_mask + ((size_t)(b * a.Hq + head) * a.Lq + rq) * nK
-                            : nullptr;
-  if (rrow && plan.causal)
-    for (int j = plan.last + 1; j < nK; ++j) rrow[j] = 2;
+  // (its address is formed where it is written, not held across the tiles)
+  const bool row_writer = a.row_mask && g == 0 && row_ok;
+  auto rrow = [&]() __attribute__((always_inline)) {
+    return a.row_mask + ((size_t)(b * a.Hq + head) * a.Lq + rq) * nK;
+  };
+  if (row_writer && plan.causal)
+    for (int j = plan.last + 1; j < nK; ++j) rrow()[j] = 2;
 
   // Issue the direct-to-LDS loads of tile j into ring stage st.  Wave w covers
   // rows [w * LOADS * ROWS_PER_LOAD, ...); lane l of load i writes LDS row
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     for (int i = 0; i < LOADS; ++i) {
       const int r = (w * LOADS + i) * ROWS_PER_LOAD + lr;
       const unsigned ro = (unsigned)min(r, rlast) * ROW;
-      const unsigned kc = pc ^ (r & 7);         // inverse of k_slot (an involution)
+      const unsigned kc = k_slot<D>(r, pc);     // inverse of k_slot (an involution)
       const unsigned vc = pc ^ ((r & 3) << 1);  // inverse of v_slot
       const int off = (w * LOADS + i) * ROWS_PER_LOAD * ROW;
       __builtin_amdgcn_global_load_lds(
@@ -179,12 +189,12 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   float lpart = 0.f;                 // this lane's half of the row's denominator
 
   // per-lane LDS offsets (the parts of the addresses that depend on the swizzle)
-  // K: row kb * 32 + l32, logical chunk 2 ks + g.  The swizzle sees only
-  // l32 & 7 and chunk bits 0..2, so four offsets cover every k-step (bit 3 of
-  // the chunk and the row block are immediate offsets).
-  int koff[4];
+  // K: row kb * 32 + l32, logical chunk 2 ks + g; the swizzle depends on the
+  // row only through l32 (the row block is an immediate offset), so one
+  // offset per k-step.
+  int koff[KS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) koff[i] = (k_slot(l32, 2 * i + g) << 4) + l32 * ROW;
+  for (int i = 0; i < KS; ++i) koff[i] = (k_slot<D>(l32, 2 * i + g) << 4) + l32 * ROW;
   // V^T: keys {4g..4g+3} and {8+4g..8+4g+3} of each 16-key step, rows
   // 16 step + 4 g + r16 / 4 (+ 8); columns 32 mb + 16 (lane / 16 & 1) +
   // 4 (r16 & 3).  The swizzle sees only the row's low two bits and chunk bits
@@ -223,8 +233,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
         u32x4_t kop[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          kop[ks] = *reinterpret_cast<const u32x4_t*>(Ks + kb * 32 * ROW + (k4 >> 2) * 128 +
-                                                      koff[ks]);
+          kop[ks] = *reinterpret_cast<const u32x4_t*>(Ks + kb * 32 * ROW + koff[k4 + ks]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), qf[k4 + ks],
@@ -258,7 +267,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     float delta = neg_inf();
     if (row_ok && tmax2 != neg_inf()) delta = (m2 == neg_inf()) ? pos_inf() : tmax2 - m2;
     const bool row_skip = delta < a.log2_thr;  // this row's own test
-    if (rrow) rrow[j] = row_skip ? 1 : 0;
+    if (row_writer) rrow()[j] = row_skip ? 1 : 0;
     delta = wave_max(delta);
     if (lane == 0) red[hh][wr] = delta;
     __syncthreads();  // red[] visible
