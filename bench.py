@@ -252,7 +252,10 @@ def bench_latent(ss, torch, args):
         torch.cuda.synchronize()
         return skip_fraction(mask)
 
-    thr, _, reachable = bisect_threshold(skip_at, args.target_skip, iters=24, tol=0.005)
+    if args.latent_threshold is not None:
+        thr, reachable = args.latent_threshold, True
+    else:
+        thr, _, reachable = bisect_threshold(skip_at, args.target_skip, iters=24, tol=0.005)
 
     def timed(th):
         for _ in range(3):
@@ -360,6 +363,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only-sparse-decode", action="store_true",
                     help="time only the sparse decode (for hardware-counter runs)")
+    ap.add_argument("--only-latent", action="store_true",
+                    help="time only the latent decode (for kernel-trace runs)")
+    ap.add_argument("--latent-threshold", type=float, default=None,
+                    help="use this latent-decode threshold instead of calibrating")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -380,6 +387,9 @@ def main():
     if args.only_sparse_decode:
         args.no_prefill = args.no_cpu = args.no_latent = True
     args.flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    if args.only_latent:
+        print(json.dumps({"latent": bench_latent(ss, torch, args)}), flush=True)
+        return
 
     dec = bench_decode(ss, torch, args)
     w, by = dec["workload"], dec["bytes"]
