@@ -20,6 +20,7 @@ from .attention import (  # noqa: F401
     lse_combine,
     n_tiles,
     prefill,
+    prefill_backward,
     skip_fraction,
     split_ranges,
     stream_pass,

@@ -396,3 +396,77 @@ def dense_decode(q, k, v, scale: float, latent_dv: int | None = None) -> np.ndar
             p = np.exp(s - s.max())
             out[b, h] = (p @ v[b, h // g]) / p.sum()
     return out
+
+
+def prefill_backward(q, k, v, do, scale: float, causal: bool, mask=None, *, tq: int = 128,
+                     tk: int = 128) -> dict:
+    """Gradients of the skip-softmax prefill with its skip decisions held fixed.
+
+    The pages train models with the sparsity on (BLASST summary page,
+    "Belangrijkste Bijdragen", the sparsity-aware training contribution) but
+    print no backward pass;
+    the plainest reading is the derivative of the forward output with the
+    decisions replayed as constants (they are a threshold test, piecewise
+    constant in the inputs).  With them fixed, row ``r`` of query tile ``i``
+    attends by plain softmax (design page, "The online-softmax pass": the
+    pass is exact over the keys it keeps) to the visible keys of the tiles
+    ``j`` with ``mask[b, h, i, j] == 0``:
+
+        P_r = softmax(scale * q_r K^T) over those keys,   O_r = P_r V
+        dV += P^T dO,   dP = dO V^T,   D_r = dO_r . O_r,
+        dS = P * (dP - D),   dQ = scale dS K,   dK += scale dS^T Q
+
+    ``mask`` u8 [B,Hq,nQ,nK] (0 computed, 1 skipped, 2 not visited), as the
+    forward wrote it; ``None`` keeps every visible tile (dense attention).
+    Query head h reads (and sends gradient to) KV head h // (Hq/Hkv).
+    Returns ``dq`` [B,Hq,Lq,D], ``dk`` [B,Hkv,Lk,D], ``dv`` [B,Hkv,Lk,Dv],
+    and the forward ``out``, ``lse`` (ln of the row's kept exponential sum,
+    -inf for a row with no kept key) and ``D`` = rowsum(dO * O).
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    B, Hq, Lq, Dq = q.shape
+    _, Hkv, Lk, _ = k.shape
+    Dv = v.shape[-1]
+    g = Hq // Hkv
+    nQ, nK = n_tiles(Lq, tq), n_tiles(Lk, tk)
+    m = None if mask is None else np.asarray(mask)
+    dq = np.zeros_like(q)
+    dk = np.zeros((B, Hkv, Lk, Dq))
+    dv = np.zeros((B, Hkv, Lk, Dv))
+    out = np.zeros((B, Hq, Lq, Dv))
+    lse = np.full((B, Hq, Lq), NEG_INF)
+    dvec = np.zeros((B, Hq, Lq))
+    keys_all = np.arange(Lk)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // g
+            for i in range(nQ):
+                rows = np.arange(i * tq, min((i + 1) * tq, Lq))
+                kept = np.zeros(Lk, bool)
+                for j in range(nK):
+                    if m is None or m[b, h, i, j] == MASK_COMPUTED:
+                        kept[j * tk:(j + 1) * tk] = True
+                vis = np.broadcast_to(kept[None, :], (len(rows), Lk)).copy()
+                if causal:
+                    vis &= keys_all[None, :] <= rows[:, None] + (Lk - Lq)
+                s = scale * (q[b, h, rows] @ k[b, hk].T)
+                s = np.where(vis, s, NEG_INF)
+                mx = s.max(axis=1, keepdims=True)
+                seen = np.isfinite(mx)[:, 0]
+                p = np.zeros_like(s)
+                if seen.any():
+                    e = np.exp(s[seen] - mx[seen])
+                    den = e.sum(axis=1, keepdims=True)
+                    p[seen] = e / den
+                    lse[b, h, rows[seen]] = (mx[seen] + np.log(den))[:, 0]
+                o = p @ v[b, hk]
+                out[b, h, rows] = o
+                dor = do[b, h, rows]
+                dp = dor @ v[b, hk].T
+                d = (dor * o).sum(axis=1)
+                ds = p * (dp - d[:, None])
+                dvec[b, h, rows] = d
+                dv[b, hk] += p.T @ dor
+                dq[b, h, rows] = scale * (ds @ k[b, hk])
+                dk[b, hk] += scale * (ds.T @ q[b, h, rows])
+    return {"dq": dq, "dk": dk, "dv": dv, "out": out, "lse": lse, "D": dvec}

@@ -89,3 +89,48 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
 def test_unmutated_battery_passes():
     for check in battery():
         check()
+
+
+# --------------------------------------------------------------------------- backward
+
+from tests import test_oracle_backward_pins as bpins  # noqa: E402
+
+BACKWARD_MUTATIONS = {
+    "softmax derivative without the row term": ("ds = p * (dp - d[:, None])", "ds = p * dp"),
+    "key gradient without the scale": ("dk[b, hk] += scale * (ds.T @ q[b, h, rows])",
+                                       "dk[b, hk] += ds.T @ q[b, h, rows]"),
+    "value gradient from dS": ("dv[b, hk] += p.T @ dor", "dv[b, hk] += ds.T @ dor"),
+    "skipped tiles kept": ("if m is None or m[b, h, i, j] == MASK_COMPUTED:",
+                           "if m is None or m[b, h, i, j] != MASK_UNVISITED:"),
+    "top-left causal alignment": ("keys_all[None, :] <= rows[:, None] + (Lk - Lq)",
+                                  "keys_all[None, :] <= rows[:, None]"),
+    "query gradient from P instead of dS": ("dq[b, h, rows] = scale * (ds @ k[b, hk])",
+                                            "dq[b, h, rows] = scale * (p @ k[b, hk])"),
+}
+
+
+def backward_battery():
+    yield lambda: bpins.test_dense_gradients_match_autograd(True, dict(Lq=130, Lk=300))
+    yield lambda: bpins.test_dense_gradients_match_autograd(False, dict(Hq=4, Hkv=2, Lq=200,
+                                                                        Lk=200))
+    yield lambda: bpins.test_skip_gradients_match_finite_differences_of_the_forward(1.0, True)
+    yield bpins.test_key_gradient_sums_to_zero
+    yield bpins.test_value_gradient_sums_to_the_output_gradient
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTATIONS))
+def test_backward_pins_catch_planted_mistake(name, monkeypatch):
+    mod = mutant(*BACKWARD_MUTATIONS[name])
+    monkeypatch.setattr(oracle, "prefill_backward", mod.prefill_backward)
+    caught = []
+    for check in backward_battery():
+        try:
+            check()
+        except AssertionError:
+            caught.append(check)
+    assert caught, f"no backward pin caught the planted mistake: {name}"
+
+
+def test_unmutated_backward_battery_passes():
+    for check in backward_battery():
+        check()
