@@ -23,6 +23,7 @@ __all__ = [
     "ss_gate_enabled", "ss_resolve_threshold", "ss_last_error", "ss_version", "library_path",
     "SSError", "TILE", "ORDERS", "mask_shape_prefill", "mask_shape_decode",
     "ss_attn_decode_paged", "GRANULARITIES", "row_mask_shape_prefill", "row_mask_shape_decode",
+    "ss_attn_prefill_backward", "ss_attn_prefill_backward_workspace_bytes",
 ]
 
 TILE = 128
@@ -52,7 +53,8 @@ class _PrefillParams(ctypes.Structure):
                 ("D", ctypes.c_int), ("Dv", ctypes.c_int), ("scale", ctypes.c_float),
                 ("threshold", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
                 ("order", ctypes.c_int), ("skip_mask_out", ctypes.c_void_p),
-                ("granularity", ctypes.c_int), ("row_mask_out", ctypes.c_void_p)]
+                ("granularity", ctypes.c_int), ("row_mask_out", ctypes.c_void_p),
+                ("lse_out", ctypes.c_void_p)]
 
 
 class _DecodeParams(ctypes.Structure):
@@ -79,6 +81,17 @@ class _DecodePagedParams(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class _PrefillBwdParams(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("skip_mask", ctypes.c_void_p), ("dq", ctypes.c_void_p),
+                ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p), ("B", ctypes.c_int),
+                ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("Lq", ctypes.c_int),
+                ("Lk", ctypes.c_int), ("D", ctypes.c_int), ("Dv", ctypes.c_int),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 SPLIT_MODES = {"chained": 0, "independent": 1}
 # who takes a skip decision: the whole row block of a tile, or every row alone
 GRANULARITIES = {"tile": 0, "row": 1}
@@ -91,6 +104,8 @@ _SIGNATURES = {
     "ss_attn_prefill": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _F, _P, _P]),
     "ss_attn_prefill_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _F, _P, _P]),
     "ss_attn_prefill_ex": (_I, [ctypes.POINTER(_PrefillParams), _P]),
+    "ss_attn_prefill_backward": (_I, [ctypes.POINTER(_PrefillBwdParams), _P]),
+    "ss_attn_prefill_backward_workspace_bytes": (_SZ, [_I, _I, _I]),
     "ss_attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _P, _SZ, _P]),
     "ss_attn_decode_ex": (_I, [ctypes.POINTER(_DecodeParams), _P]),
     "ss_attn_decode_paged": (_I, [ctypes.POINTER(_DecodePagedParams), _P]),
@@ -188,13 +203,14 @@ def _granularity(granularity, row_mask, shape):
 
 def ss_attn_prefill_ex(q, k, v, out=None, *, scale=None, causal=False, threshold=0.0,
                        skip_mask=None, order="ascending", granularity="tile", row_mask=None,
-                       stream=None):
+                       lse=None, stream=None):
     """Skip-softmax prefill: q[B,Hq,Lq,D], k[B,Hkv,Lk,D], v[B,Hkv,Lk,Dv] on the GPU
     (all bf16 or all fp32).  Returns ``out`` [B,Hq,Lq,Dv]; fills ``skip_mask``
     (u8 [B,Hq,ceil(Lq/128),ceil(Lk/128)]) when given.  ``granularity="row"``
     lets every query row decide alone; ``row_mask`` (u8
-    [B,Hq,Lq,ceil(Lk/128)]) then receives the per-row decisions.  Asynchronous
-    on ``stream`` (default: the current stream)."""
+    [B,Hq,Lq,ceil(Lk/128)]) then receives the per-row decisions.  ``lse``
+    (fp32 [B,Hq,Lq]) receives each row's log-sum-exp over its kept keys.
+    Asynchronous on ``stream`` (default: the current stream)."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, L, D]")
     B, Hq, Lq, D = q.shape
@@ -219,9 +235,14 @@ def ss_attn_prefill_ex(q, k, v, out=None, *, scale=None, causal=False, threshold
     if order not in ORDERS:
         raise ValueError(f"order must be one of {sorted(ORDERS)}")
     gran, rptr = _granularity(granularity, row_mask, row_mask_shape_prefill(B, Hq, Lq, Lk))
+    lptr = None
+    if lse is not None:
+        if tuple(lse.shape) != (B, Hq, Lq):
+            raise ValueError(f"lse must be {(B, Hq, Lq)}")
+        lptr = _dev(lse, "lse", torch.float32)
     p = _PrefillParams(_dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _dev(out, "out", dt),
                        B, Hq, Hkv, Lq, Lk, D, Dv, float(scale), float(threshold), int(bool(causal)),
-                       _DTYPE[dt], ORDERS[order], mptr, gran, rptr)
+                       _DTYPE[dt], ORDERS[order], mptr, gran, rptr, lptr)
     _check(lib().ss_attn_prefill_ex(ctypes.byref(p), _stream(stream, q.device)))
     return out
 
@@ -242,6 +263,64 @@ def ss_attn_prefill_f32(q, k, v, out=None, *, scale=None, causal=False, threshol
         raise TypeError("ss_attn_prefill_f32 takes fp32 tensors")
     return ss_attn_prefill_ex(q, k, v, out, scale=scale, causal=causal, threshold=threshold,
                               skip_mask=skip_mask, stream=stream)
+
+
+def ss_attn_prefill_backward_workspace_bytes(B, Hq, Lq) -> int:
+    return int(lib().ss_attn_prefill_backward_workspace_bytes(B, Hq, Lq))
+
+
+def ss_attn_prefill_backward(q, k, v, out, dout, lse, skip_mask=None, *, scale=None,
+                             causal=False, dq=None, dk=None, dv=None, workspace=None,
+                             stream=None):
+    """Skip-aware backward of the bf16 prefill: gradients of ``out`` with the
+    forward's skip decisions held fixed.  ``out`` and ``lse`` (fp32 [B,Hq,Lq])
+    come from the forward call (``ss_attn_prefill_ex(..., lse=...)``), ``dout``
+    is dL/dout, ``skip_mask`` the forward's tile mask (None: dense attention).
+    ``scale`` and ``causal`` must be the forward's.  Returns ``(dq, dk, dv)``
+    (bf16, allocated when not given).  Asynchronous on ``stream``."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, L, D]")
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lk, Dk = k.shape
+    Dv = v.shape[3]
+    if (Bk, Dk) != (B, D) or tuple(v.shape[:3]) != (B, Hkv, Lk):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for name, t in (("out", out), ("dout", dout)):
+        if tuple(t.shape) != (B, Hq, Lq, Dv):
+            raise ValueError(f"{name} must be {(B, Hq, Lq, Dv)}")
+    if tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError(f"lse must be {(B, Hq, Lq)}")
+    dt = torch.bfloat16
+    if q.dtype != dt:
+        raise TypeError("ss_attn_prefill_backward takes bf16 tensors")
+    mptr = None
+    if skip_mask is not None:
+        if tuple(skip_mask.shape) != mask_shape_prefill(B, Hq, Lq, Lk):
+            raise ValueError(f"skip_mask must be {mask_shape_prefill(B, Hq, Lq, Lk)}")
+        mptr = _dev(skip_mask, "skip_mask", torch.uint8)
+    if dq is None:
+        dq = torch.empty((B, Hq, Lq, D), dtype=dt, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, Hkv, Lk, D), dtype=dt, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, Hkv, Lk, Dv), dtype=dt, device=q.device)
+    for name, t, shp in (("dq", dq, (B, Hq, Lq, D)), ("dk", dk, (B, Hkv, Lk, D)),
+                         ("dv", dv, (B, Hkv, Lk, Dv))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be {shp}")
+    if workspace is None:
+        need = ss_attn_prefill_backward_workspace_bytes(B, Hq, Lq)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    p = _PrefillBwdParams(_dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
+                          _dev(out, "out", dt), _dev(dout, "dout", dt),
+                          _dev(lse, "lse", torch.float32), mptr, _dev(dq, "dq", dt),
+                          _dev(dk, "dk", dt), _dev(dv, "dv", dt), B, Hq, Hkv, Lq, Lk, D, Dv,
+                          float(scale), int(bool(causal)), _DTYPE[dt], _dev(workspace, "workspace"),
+                          workspace.numel() * workspace.element_size())
+    _check(lib().ss_attn_prefill_backward(ctypes.byref(p), _stream(stream, q.device)))
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------- decode

@@ -30,8 +30,9 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
 # ... except where the accumulators alone fill the 256 architectural VGPRs:
 # the latent decode keeps a [512 x 32] fp32 output block per wave in the
-# accumulation registers.
-AGPR_FORM = {"decode_mla.hip"}
+# accumulation registers, the backward's dK/dV kernel the dK^T and dV^T
+# blocks of 32 keys.
+AGPR_FORM = {"decode_mla.hip", "prefill_bwd_dkdv.hip"}
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 

@@ -262,6 +262,7 @@ int ss_attn_prefill_ex(const ss_prefill_params* p, hipStream_t stream) {
   a.order = p->order;
   a.per_row = p->granularity == SS_SKIP_ROW;
   a.row_mask = p->row_mask_out;
+  a.lse = p->lse_out;
   hipError_t e = p->dtype == SS_DTYPE_BF16 ? ssattn::launch_prefill_bf16(a, stream)
                                            : ssattn::launch_prefill_f32(a, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
@@ -290,6 +291,64 @@ int ss_decode_num_splits(int B, int Hq, int Hkv, int Lk, int D, int Dv) {
     return 0;
   const bool latent = decode_kernel(D, Dv, Hq / Hkv, false) == DecodeKernel::kNone && Dv <= D;
   return auto_splits(B, Hq, Hkv, Lk, D, Dv, latent);
+}
+
+size_t ss_attn_prefill_backward_workspace_bytes(int B, int Hq, int Lq) {
+  if (B <= 0 || Hq <= 0 || Lq <= 0 || Lq > kMaxLen) return 0;
+  const size_t nQ = ((size_t)Lq + SS_TILE_ROWS - 1) / SS_TILE_ROWS;
+  return align256((size_t)B * Hq * nQ * 2 * SS_TILE_ROWS * sizeof(float));
+}
+
+int ss_attn_prefill_backward(const ss_prefill_bwd_params* p, hipStream_t stream) {
+  if (!p) return fail(SS_ERR_INVALID_ARG, "params is null");
+  if (!p->q || !p->k || !p->v || !p->out || !p->dout || !p->lse || !p->dq || !p->dk || !p->dv)
+    return fail(SS_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk and dv must be non-null");
+  if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Lq <= 0 || p->Lk <= 0 || p->D <= 0 ||
+      p->Dv <= 0)
+    return fail(SS_ERR_INVALID_ARG, "sizes must be positive");
+  if (p->Lq > kMaxLen || p->Lk > kMaxLen)
+    return fail(SS_ERR_INVALID_ARG, "sequence lengths above %d are not supported", kMaxLen);
+  if (p->Hq % p->Hkv) return fail(SS_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)",
+                                  p->Hq, p->Hkv);
+  if (int rc = check_scale(p->scale)) return rc;
+  if (p->dtype != SS_DTYPE_BF16)
+    return fail(p->dtype == SS_DTYPE_F32 ? SS_ERR_UNSUPPORTED : SS_ERR_INVALID_ARG,
+                "the prefill backward supports dtype bf16 only (got %d)", p->dtype);
+  if (!ssattn::prefill_bwd_supported(p->D, p->Dv))
+    return fail(SS_ERR_UNSUPPORTED, "the prefill backward supports D == Dv in {64, 128} (got %d, %d)",
+                p->D, p->Dv);
+  const size_t need = ss_attn_prefill_backward_workspace_bytes(p->B, p->Hq, p->Lq);
+  if (!p->workspace || p->workspace_bytes < need)
+    return fail(SS_ERR_WORKSPACE, "prefill backward workspace needs %zu bytes (got %zu%s)", need,
+                p->workspace_bytes, p->workspace ? "" : ", null");
+  ssattn::PrefillBwdArgs a{};
+  a.q = p->q;
+  a.k = p->k;
+  a.v = p->v;
+  a.out = p->out;
+  a.dout = p->dout;
+  a.lse = p->lse;
+  a.mask = p->skip_mask;
+  a.dq = p->dq;
+  a.dk = p->dk;
+  a.dv = p->dv;
+  a.rowstat = static_cast<float*>(p->workspace);
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.Lq = p->Lq;
+  a.Lk = p->Lk;
+  a.D = p->D;
+  a.Dv = p->Dv;
+  a.scale = p->scale;
+  a.causal = p->causal != 0;
+  hipError_t e = ssattn::launch_prefill_bwd_rowstat(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill backward row statistics launch");
+  e = ssattn::launch_prefill_bwd_dkdv(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill backward dK/dV launch");
+  e = ssattn::launch_prefill_bwd_dq(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill backward dQ launch");
+  return ok();
 }
 
 size_t ss_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lk, int D, int Dv,

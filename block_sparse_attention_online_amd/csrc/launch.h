@@ -26,6 +26,7 @@ struct PrefillArgs {
   // row_mask (may be null) is u8 [B, Hq, Lq, nK].
   int per_row;
   uint8_t* row_mask;
+  float* lse;  // may be null: [B, Hq, Lq] ln of the row's kept exponential sum
 };
 
 // Arguments of one split-KV decode launch.
@@ -69,10 +70,33 @@ struct DecodeArgs {
   uint8_t* row_mask;
 };
 
+// Arguments of the backward launches of a bf16 prefill.
+struct PrefillBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;   // forward output O [B, Hq, Lq, Dv]
+  const void* dout;  // dL/dO           [B, Hq, Lq, Dv]
+  const float* lse;  // forward log-sum-exp (natural log) [B, Hq, Lq]
+  const uint8_t* mask;  // forward skip mask [B, Hq, nQ, nK], or null: every visible tile
+  void* dq;
+  void* dk;
+  void* dv;
+  float* rowstat;  // workspace [B, Hq, nQ, 2, 128]: lse * log2(e) (+inf: no kept key), dO . O
+  int B, Hq, Hkv, Lq, Lk, D, Dv;
+  float scale;
+  int causal;
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 bool prefill_bf16_supported(int D, int Dv);
 bool prefill_f32_supported(int D, int Dv);
+
+bool prefill_bwd_supported(int D, int Dv);
+hipError_t launch_prefill_bwd_rowstat(const PrefillBwdArgs& a, hipStream_t s);
+hipError_t launch_prefill_bwd_dkdv(const PrefillBwdArgs& a, hipStream_t s);
+hipError_t launch_prefill_bwd_dq(const PrefillBwdArgs& a, hipStream_t s);
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_gqa_paged(const DecodeArgs& a, hipStream_t s);

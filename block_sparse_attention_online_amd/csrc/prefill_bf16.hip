@@ -352,6 +352,8 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   // ---- epilogue: O / l, lane holds columns 32 mb + 8 (i/4) + 4 g + i%4 of row rq
   const float l = sum_xor32(lpart);
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (a.lse && row_ok && g == 0)
+    a.lse[(size_t)(b * a.Hq + head) * a.Lq + rq] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : neg_inf();
   unsigned short* op = static_cast<unsigned short*>(a.out) + ((size_t)(b * a.Hq + head) * a.Lq) * D;
   if (row_ok) {
 #pragma unroll

@@ -132,6 +132,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
     m2 = m2_new;
   }
 
+  if (row_ok && half == 0 && a.lse)
+    a.lse[(size_t)(b * a.Hq + h) * a.Lq + row] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : neg_inf();
   if (row_ok) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll

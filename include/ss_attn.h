@@ -56,7 +56,7 @@ typedef enum {
   SS_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad threshold, Hq % Hkv != 0 */
   SS_ERR_UNSUPPORTED = -2, /* head dimensions or grouping without a kernel */
   SS_ERR_HIP = -3,         /* a HIP launch failed; see ss_last_error() */
-  SS_ERR_WORKSPACE = -4    /* decode workspace missing or too small */
+  SS_ERR_WORKSPACE = -4    /* workspace missing or too small */
 } ss_status;
 
 typedef enum { SS_FACTOR_DIRECT = 0, SS_FACTOR_CALIBRATED = 1 } ss_factor_mode;
@@ -118,7 +118,10 @@ int ss_attn_prefill_f32(const float* q, const float* k, const float* v, float* o
 /* Full form: the two calls above are this one with dtype BF16 / F32, order
  * ASCENDING and granularity SS_SKIP_TILE.  row_mask_out (SS_SKIP_ROW only,
  * else it must be NULL): u8 [B, Hq, Lq, ceil(Lk/128)], every row's decision
- * per key tile (2 for tiles its query tile does not visit), or NULL. */
+ * per key tile (2 for tiles its query tile does not visit), or NULL.
+ * lse_out: fp32 [B, Hq, Lq] or NULL; row r receives ln of its sum of
+ * exp(scale q_r . k_c) over the keys it kept (-inf when it kept none), what
+ * ss_attn_prefill_backward needs to rebuild the row's weights. */
 typedef struct {
   const void* q;
   const void* k;
@@ -133,9 +136,63 @@ typedef struct {
   uint8_t* skip_mask_out;
   int granularity;       /* ss_granularity */
   uint8_t* row_mask_out; /* SS_SKIP_ROW: u8 [B, Hq, Lq, ceil(Lk/128)] or NULL */
+  float* lse_out;        /* fp32 [B, Hq, Lq] or NULL */
 } ss_prefill_params;
 
 int ss_attn_prefill_ex(const ss_prefill_params* p, hipStream_t stream);
+
+/*
+ * Skip-aware backward of the prefill.  The pages train with the sparsity on
+ * (BLASST summary, "Belangrijkste Bijdragen": sparsity-aware training) and
+ * give no backward pass; this is the derivative of the forward with its skip
+ * decisions held fixed.  With them fixed, row r of query tile i attends by
+ * plain softmax (design page, "The online-softmax pass") to the visible keys
+ * of the key tiles j whose skip_mask byte for (b, h, i, j) is 0:
+ *     P = exp(scale Q K^T - lse),  dV = P^T dO,  dP = dO V^T,
+ *     Delta_r = dO_r . O_r,  dS = P (dP - Delta),
+ *     dQ = scale dS K,  dK = scale dS^T Q
+ * (dK and dV of a KV head sum over the query heads that read it).  Pairs the
+ * forward skipped or did not visit contribute nothing and run no product.
+ *
+ *   q, k, v, out, dout   as the forward: q [B,Hq,Lq,D], k [B,Hkv,Lk,D],
+ *                        v [B,Hkv,Lk,Dv]; out = the forward's output and
+ *                        dout = dL/dout, both [B,Hq,Lq,Dv]; bf16
+ *   lse        fp32 [B,Hq,Lq], the forward's lse_out
+ *   skip_mask  u8 [B,Hq,ceil(Lq/128),ceil(Lk/128)], the forward's
+ *              skip_mask_out (SS_SKIP_TILE), or NULL for every visible tile
+ *              (the derivative of dense attention)
+ *   dq [B,Hq,Lq,D], dk [B,Hkv,Lk,D], dv [B,Hkv,Lk,Dv]  bf16 (written; every
+ *              element, zeros where no kept pair reaches it)
+ *   workspace  caller-owned device memory of at least
+ *              ss_attn_prefill_backward_workspace_bytes(B, Hq, Lq) bytes
+ *              (per-row statistics; contents on entry do not matter)
+ *
+ * scale, causal and the sizes must be those of the forward call.  Supported:
+ * dtype SS_DTYPE_BF16, D == Dv in {64, 128}.  Three kernels on `stream`
+ * (row statistics, then dK/dV, then dQ); no atomics, so the result is the
+ * same bit for bit on every run.
+ */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  const uint8_t* skip_mask;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Lq, Lk, D, Dv;
+  float scale;
+  int causal;
+  int dtype; /* ss_dtype: SS_DTYPE_BF16 */
+  void* workspace;
+  size_t workspace_bytes;
+} ss_prefill_bwd_params;
+
+size_t ss_attn_prefill_backward_workspace_bytes(int B, int Hq, int Lq);
+int ss_attn_prefill_backward(const ss_prefill_bwd_params* p, hipStream_t stream);
 
 /* ------------------------------------------------------------------ decode */
 

@@ -12,6 +12,7 @@ from .generators import (  # noqa: F401
     clustered_decode,
     clustered_prefill,
     gumbel_decode,
+    output_gradient,
     video_dit_field,
 )
 from .workloads import WORKLOADS, Workload, make_inputs  # noqa: F401

@@ -299,3 +299,17 @@ def gumbel_decode(seed: int, B: int, Hq: int, Hkv: int, Lk: int, D: int, Dv: int
 
     _for_units([(b, hk) for b in range(B) for hk in range(Hkv)], unit)
     return {"q": q, "k": k, "v": v}
+
+
+def output_gradient(seed: int, B: int, H: int, L: int, Dv: int, dtype: str = "bf16") -> torch.Tensor:
+    """dL/dout for a backward call: i.i.d. N(0, 1) [B, H, L, Dv], one stream
+    per (b, head) so a slice of heads draws the same values at any size."""
+    out = torch.empty((B, H, L, Dv), dtype=_torch_dtype(dtype))
+
+    def unit(bh):
+        b, h = bh
+        out[b, h] = _to_tensor(_unit_rng(seed, b, h).standard_normal((L, Dv), dtype=np.float32),
+                               dtype)
+
+    _for_units([(b, h) for b in range(B) for h in range(H)], unit)
+    return out

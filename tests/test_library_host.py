@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["ss_attn_prefill", "ss_attn_prefill_f32", "ss_attn_prefill_ex", "ss_attn_decode",
               "ss_attn_decode_ex", "ss_attn_decode_partial", "ss_attn_decode_combine",
-              "ss_attn_decode_paged",
+              "ss_attn_decode_paged", "ss_attn_prefill_backward",
+              "ss_attn_prefill_backward_workspace_bytes",
               "ss_attn_decode_workspace_bytes", "ss_decode_num_splits", "ss_factor",
               "ss_threshold", "ss_gate_enabled", "ss_resolve_threshold", "ss_last_error",
               "ss_version"]:
@@ -215,6 +216,37 @@ def test_prefill_rejects_bad_granularity(ss):
     assert "row_mask_out" in ss.ss_last_error()
 
 
+def test_backward_workspace_bytes(ss):
+    # per (batch, head, 128-row query tile): 128 lse values and 128 row dots, fp32
+    assert ss.ss_attn_prefill_backward_workspace_bytes(1, 32, 16384) == 32 * 128 * 1024
+    assert ss.ss_attn_prefill_backward_workspace_bytes(2, 3, 129) == 2 * 3 * 2 * 1024
+    assert ss.ss_attn_prefill_backward_workspace_bytes(1, 1, 1) == 1024
+    for bad in [(0, 1, 1), (1, 0, 1), (1, 1, 0), (1, 1, (1 << 24) + 1)]:
+        assert ss.ss_attn_prefill_backward_workspace_bytes(*bad) == 0
+
+
+def backward_call(ss, **over):
+    a = dict(q=0x1000, k=0x1000, v=0x1000, out=0x1000, dout=0x1000, lse=0x1000, skip_mask=None,
+             dq=0x1000, dk=0x1000, dv=0x1000, B=1, Hq=4, Hkv=2, Lq=256, Lk=256, D=128, Dv=128,
+             scale=0.1, causal=1, dtype=0, workspace=0x1000, workspace_bytes=1 << 30)
+    a.update(over)
+    p = ss._PrefillBwdParams(*[a[f] for f, _ in ss._PrefillBwdParams._fields_])
+    return ss.lib().ss_attn_prefill_backward(ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), -1), (dict(dout=None), -1), (dict(lse=None), -1), (dict(dk=None), -1),
+    (dict(B=0), -1), (dict(Lk=-1), -1), (dict(Hq=3), -1), (dict(scale=0.0), -1),
+    (dict(scale=float("nan")), -1), (dict(Lq=(1 << 24) + 1), -1), (dict(dtype=7), -1),
+    (dict(dtype=1), -2), (dict(D=96, Dv=96), -2), (dict(D=128, Dv=64), -2),
+    (dict(workspace=None), -4), (dict(workspace_bytes=4 * 2 * 1024 - 1), -4),
+])
+def test_backward_rejects_before_launch(ss, over, code):
+    assert backward_call(ss, **over) == code
+    assert ss.ss_last_error()
+    assert ss.lib().ss_attn_prefill_backward(None, None) == -1
+
+
 def test_struct_layouts_match_header(ss, tmp_path):
     """Every field of the parameter structs sits at the offset the C compiler
     gives it in include/ss_attn.h (the binding fills them by position)."""
@@ -225,7 +257,8 @@ def test_struct_layouts_match_header(ss, tmp_path):
     if gcc is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
         pytest.skip("needs gcc and the HIP headers")
     structs = {"ss_prefill_params": ss._PrefillParams, "ss_decode_params": ss._DecodeParams,
-               "ss_decode_paged_params": ss._DecodePagedParams}
+               "ss_decode_paged_params": ss._DecodePagedParams,
+               "ss_prefill_bwd_params": ss._PrefillBwdParams}
     lines = ['#include "ss_attn.h"', "#include <stdio.h>", "#include <stddef.h>",
              "int main(void) {"]
     for name, cls in structs.items():
