@@ -24,7 +24,8 @@ of those step times.  ``warm_value`` is the same decode run back to back
 
 ``roofline`` is for the decode kernel alone; ``cpu_baseline`` times the fp64
 CPU oracle on a bounded sample of the same decode.  ``latent`` is the
-latent-cache decode (B8, 128 heads, 576-wide rows, 131072 keys).
+latent-cache decode (B8, 128 heads, 576-wide rows, 131072 keys);
+``backward`` the skip-aware backward of the causal GQA prefill.
 
 Usage: python bench.py [--steps K] [--warmup W] [--target-skip 0.7]
        python bench.py --copy-probe       (a plain 1 GiB device copy, for
@@ -225,6 +226,72 @@ def bench_prefill(ss, torch, args, r, order):
     return res
 
 
+# --------------------------------------------------------------------------- prefill backward
+
+def bench_backward(ss, torch, args):
+    """Skip-aware backward of the causal GQA prefill (B1 Hq32 Hkv8 L16384
+    D128, clustered tile generator r=3): the forward at the threshold runs
+    once, untimed, for the skip mask and lse; then the backward is timed
+    replaying that mask, against the same backward with no mask (every
+    visible tile: dense attention's gradients).  Algorithmic flops: the five
+    products of a kept 128x128 tile pair (S, dP, dV, dK, dQ), 2*128*128*D
+    each; the kernels run seven (S and dP are recomputed for dQ)."""
+    from synth import WORKLOADS, make_inputs, output_gradient
+
+    w = WORKLOADS["gqa_prefill_16k"]
+    x = make_inputs(w)
+    q, k, v = (x[n].cuda() for n in "qkv")
+    do = output_gradient(9, w.B, w.Hq, w.Lq, w.Dv).cuda()
+    out = torch.empty_like(q)
+    mask = torch.empty(ss.mask_shape_prefill(w.B, w.Hq, w.Lq, w.Lk), dtype=torch.uint8,
+                       device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ss.ss_attn_prefill_backward_workspace_bytes(w.B, w.Hq, w.Lq),
+                     dtype=torch.uint8, device="cuda")
+    thr = args.backward_threshold
+    ss.ss_attn_prefill_ex(q, k, v, out, scale=w.scale, causal=True, threshold=thr,
+                          skip_mask=mask, lse=lse, order="diag_first")
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    visited, kept = int((m != 2).sum()), int((m == 0).sum())
+
+    def timed(use_mask):
+        def run():
+            ss.ss_attn_prefill_backward(q, k, v, out, do, lse, mask if use_mask else None,
+                                        scale=w.scale, causal=True, dq=dq, dk=dk, dv=dv,
+                                        workspace=ws)
+        for _ in range(max(2, args.warmup // 4)):
+            run()
+        torch.cuda.synchronize()
+        steps = max(5, args.steps // 5)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in evs:
+            evict_caches(args.flush)
+            e[0].record()
+            run()
+            e[1].record()
+        torch.cuda.synchronize()
+        return sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+
+    dense_ms = timed(False)
+    ms = timed(True)
+    per_pair = 5 * 2 * 128 * 128 * w.D
+    tf = per_pair * kept / ms / 1e9
+    tf_d = per_pair * visited / dense_ms / 1e9
+    res = {"workload": "gqa_prefill_16k (B1 Hq32 Hkv8 L16384 D128 causal), clustered tile "
+                       "r=3, dO ~ N(0,1)",
+           "threshold": thr, "order": "diag_first",
+           "skip_fraction": round(1 - kept / visited, 4),
+           "ms": round(ms, 4), "dense_ms": round(dense_ms, 4),
+           "speedup_vs_dense": round(dense_ms / ms, 3),
+           "tflops_algorithmic": round(tf, 1), "dense_tflops_algorithmic": round(tf_d, 1),
+           "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+           "tflops_executed": round(tf * 7 / 5, 1)}
+    log(f"[backward] {res}")
+    return res
+
+
 # --------------------------------------------------------------------------- latent decode
 
 def bench_latent(ss, torch, args):
@@ -367,6 +434,11 @@ def main():
                     help="time only the latent decode (for kernel-trace runs)")
     ap.add_argument("--latent-threshold", type=float, default=None,
                     help="use this latent-decode threshold instead of calibrating")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="time only the skip-aware prefill backward")
+    ap.add_argument("--backward-threshold", type=float, default=1.0,
+                    help="forward threshold whose skip mask the backward replays")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -385,10 +457,13 @@ def main():
         copy_probe(torch)
         return
     if args.only_sparse_decode:
-        args.no_prefill = args.no_cpu = args.no_latent = True
+        args.no_prefill = args.no_cpu = args.no_latent = args.no_backward = True
     args.flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     if args.only_latent:
         print(json.dumps({"latent": bench_latent(ss, torch, args)}), flush=True)
+        return
+    if args.only_backward:
+        print(json.dumps({"backward": bench_backward(ss, torch, args)}), flush=True)
         return
 
     dec = bench_decode(ss, torch, args)
@@ -432,6 +507,8 @@ def main():
                            "wide_gap": bench_prefill(ss, torch, args, 9.0, "diag_first")}
     if not args.no_latent:
         line["latent"] = bench_latent(ss, torch, args)
+    if not args.no_backward:
+        line["backward"] = bench_backward(ss, torch, args)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -79,6 +79,18 @@ __device__ __forceinline__ int bw_tr_off(int lane, int mb, int hi) {
   return R * 2 * D + (bw_slot<D>(R, c) << 4) + (r16 & 1) * 8;
 }
 
+// The swizzle is an XOR of chunk bits with row bits, so the offsets of the
+// other k-steps (row reads) and column blocks / halves (transpose reads)
+// follow from the first by XOR with constants: one register per kind.
+//   bw_row_off<D>(l, ks)     == bw_row_off<D>(l, 0) ^ (ks << 5)
+//   bw_tr_off<D>(l, mb, hi)  == bw_tr_off<D>(l, 0, 0) ^ bw_tr_xor<D>(mb, hi)
+template <int D>
+__device__ __forceinline__ constexpr int bw_tr_xor(int mb, int hi) {
+  // hi moves the rows by 8 (bit 11 of the offset for D = 128, bit 10 for
+  // D = 64) and flips bit 1 of the swizzle term ((R >> 2) & 3 gains 2)
+  return (mb << 6) ^ (hi << 5) ^ (hi << (D == 128 ? 11 : 10));
+}
+
 // Transpose read of 8 rows (lo and hi halves) at `p + off_lo` / `p + off_hi`.
 __device__ __forceinline__ bf16x8_t bw_tr_read(const unsigned char* p, int off_lo, int off_hi) {
   const bw_s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_s16x4_t*)(p + off_lo));

@@ -114,14 +114,10 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
       dva[mb][i] = 0.f;
     }
 
-  int roff[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) roff[ks] = bw_row_off<D>(lane, ks);
-  int toff[MB][2];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = bw_tr_off<D>(lane, mb, hi);
+  // LDS offsets of this lane's row and transpose reads (k-step 0, column
+  // block 0); the others follow by XOR with constants
+  const int roff0 = bw_row_off<D>(lane, 0);
+  const int toff0 = bw_tr_off<D>(lane, 0, 0);
 
   const float c2 = a.scale * kLog2e;
 
@@ -142,6 +138,129 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
     }
   };
 
+  // Rows of a tile that do not see this lane's key: r < rmin (causal: the key
+  // is visible to row r iff key <= r + shift), every row when the key lies
+  // past Lk.  The +-2^30 sentinels leave room to subtract a row index
+  // (< 2^24) without overflow.
+  const int rmin = !key_ok ? (1 << 30) : (a.causal ? key - shift : -(1 << 30));
+
+  // The products of one pair from its ring stage, as a software pipeline over
+  // the tile's four 32-row blocks.  With one wave per SIMD nothing else hides
+  // latency, so every block runs four stages of eight MFMAs, each interleaved
+  // with the work the next stage needs:
+  //   S  = Q K^T    | LDS reads: dO rows, the rows' lse2
+  //   dP = dO V^T   | VALU: P = exp2(S c2 - lse2) -> bf16; LDS: dO^T, Delta
+  //   dV^T += dO^T P| VALU: dS = P (dP - Delta) -> bf16; LDS: Q^T
+  //   dK^T += Q^T dS| LDS: Q rows of the next block
+  // Scheduling barriers keep the compiler from hoisting a stage's reads
+  // further (their registers would not fit).  `tlim`: the row offset within
+  // the tile, minus 4 g, below which this lane's P is 0 (-2^30 when every
+  // row sees every key of the wave's block).
+  auto pair_body = [&](int tlim, const unsigned char* Qs, const unsigned char* Ds,
+                       const float* Rs) {
+    u32x4_t qa[KS], da[KS];
+    bf16x8_t tv[2][MB], tq[2][MB];
+    f32x4_t l4[4], d4[4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const u32x4_t*>(Qs + (roff0 ^ (ks << 5)));
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      // ---- stage 1: S for rows 32 rb .. + 32 (accumulator: column = key,
+      // rows 8 (e / 4) + 4 g + e % 4)
+      f32x16_t sacc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[ks]), kf[ks], sacc, 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        da[ks] = *reinterpret_cast<const u32x4_t*>(Ds + rb * 32 * ROW + (roff0 ^ (ks << 5)));
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        l4[q4] = *reinterpret_cast<const f32x4_t*>(Rs + rb * 32 + 8 * q4 + 4 * g);
+#pragma unroll
+      for (int x = 0; x < KS; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- stage 2: dP; P from S
+      f32x16_t dacc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dacc[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da[ks]), vf[ks], dacc, 0, 0, 0);
+      float pv[16];
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        const float pe = fast_exp2(fmaf(sacc[ii], c2, -l4[ii >> 2][ii & 3]));
+        pv[ii] = rb * 32 + 8 * (ii >> 2) + (ii & 3) < tlim ? 0.f : pe;
+      }
+      bf16x8_t pb[2];
+      bw_pack_b(pv, pb);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          tv[h][mb] = bw_tr_read(Ds + (rb * 32 + 16 * h) * ROW, toff0 ^ bw_tr_xor<D>(mb, 0), toff0 ^ bw_tr_xor<D>(mb, 1));
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        d4[q4] = *reinterpret_cast<const f32x4_t*>(Rs + kTile + rb * 32 + 8 * q4 + 4 * g);
+#pragma unroll
+      for (int x = 0; x < KS; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- stage 3: dV^T += dO^T P; dS from dP
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          dva[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tv[h][mb], pb[h], dva[mb], 0, 0, 0);
+      float sv[16];
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) sv[ii] = pv[ii] * (dacc[ii] - d4[ii >> 2][ii & 3]);
+      bf16x8_t sb[2];
+      bw_pack_b(sv, sb);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          tq[h][mb] = bw_tr_read(Qs + (rb * 32 + 16 * h) * ROW, toff0 ^ bw_tr_xor<D>(mb, 0), toff0 ^ bw_tr_xor<D>(mb, 1));
+#pragma unroll
+      for (int x = 0; x < 2 * MB; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- stage 4: dK^T += Q^T dS; Q rows of the next block
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          dka[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[h][mb], sb[h], dka[mb], 0, 0, 0);
+      if (rb < 3) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qa[ks] = *reinterpret_cast<const u32x4_t*>(Qs + (rb + 1) * 32 * ROW + (roff0 ^ (ks << 5)));
+      }
+#pragma unroll
+      for (int x = 0; x < 2 * MB; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // One pair; Qs/Ds/Rs: its stage, Qn/Dn/Rn: the other stage.
   auto step = [&](int t, int n, const unsigned char* Qs, const unsigned char* Ds, const float* Rs,
                   unsigned char* Qn, unsigned char* Dn, float* Rn) {
@@ -150,67 +269,10 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
     __syncthreads();
     if (t + 1 < n) issue(__builtin_amdgcn_readfirstlane(plist[t + 1]), Qn, Dn, Rn);
     const int p = __builtin_amdgcn_readfirstlane(plist[t]);
-    const int i = i_min + p % nI;
-    const int r0 = i * kTile;
+    const int r0 = (i_min + p % nI) * kTile;
     // every key of this wave's block visible to every row of the tile?
     const bool full = (j0 + w * 32 + 32 <= a.Lk) && (!a.causal || j0 + w * 32 + 31 <= r0 + shift);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      // ---- S and dP for rows 32 rb .. + 32 (accumulator: column = key, rows
-      // 8 (e / 4) + 4 g + e % 4)
-      f32x16_t s, dp;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[e] = 0.f;
-        dp[e] = 0.f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t qa = *reinterpret_cast<const u32x4_t*>(Qs + rb * 32 * ROW + roff[ks]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), kf[ks], s, 0, 0, 0);
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t da = *reinterpret_cast<const u32x4_t*>(Ds + rb * 32 * ROW + roff[ks]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da), vf[ks], dp, 0, 0, 0);
-      }
-      // ---- P = exp2(S c2 - lse2), dS = P (dP - Delta)
-      float pv[16], sv[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int rr = rb * 32 + 8 * q4 + 4 * g;
-        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(Rs + rr);
-        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(Rs + kTile + rr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ii = 4 * q4 + e;
-          float pe = fast_exp2(fmaf(s[ii], c2, -l4[e]));
-          if (!full) {
-            const int row = r0 + rr + e;
-            if (!key_ok || (a.causal && key > row + shift)) pe = 0.f;
-          }
-          pv[ii] = pe;
-          sv[ii] = pe * (dp[ii] - d4[e]);
-        }
-      }
-      bf16x8_t pb[2], sb[2];
-      bw_pack_b(pv, pb);
-      bw_pack_b(sv, sb);
-      // ---- dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row steps
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const unsigned char* dt = Ds + (rb * 32 + 16 * h) * ROW;
-        const unsigned char* qt = Qs + (rb * 32 + 16 * h) * ROW;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          dva[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              bw_tr_read(dt, toff[mb][0], toff[mb][1]), pb[h], dva[mb], 0, 0, 0);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          dka[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              bw_tr_read(qt, toff[mb][0], toff[mb][1]), sb[h], dka[mb], 0, 0, 0);
-      }
-    }
+    pair_body(full ? -(1 << 30) : rmin - r0 - 4 * g, Qs, Ds, Rs);
   };
 
   int next = 0;  // first candidate pair not yet scanned

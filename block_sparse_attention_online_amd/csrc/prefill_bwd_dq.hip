@@ -151,14 +151,10 @@ __global__ __launch_bounds__(64 * kDqRowWaves * NH, 1) void bwd_dq_kernel(Prefil
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqa[mb][i] = 0.f;
 
-  int roff[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) roff[ks] = bw_row_off<D>(lane, ks);
-  int toff[MB][2];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = bw_tr_off<D>(lane, mb, hi);
+  // LDS offsets of this lane's row and transpose reads (k-step 0, column
+  // block 0); the others follow by XOR with constants
+  const int roff0 = bw_row_off<D>(lane, 0);
+  const int toff0 = bw_tr_off<D>(lane, 0, 0);
 
   const float c2 = a.scale * kLog2e;
   const unsigned char* kbase = static_cast<const unsigned char*>(a.k) +
@@ -197,7 +193,7 @@ __global__ __launch_bounds__(64 * kDqRowWaves * NH, 1) void bwd_dq_kernel(Prefil
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(Ks + kb * 32 * ROW + roff[ks]);
+        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(Ks + kb * 32 * ROW + (roff0 ^ (ks << 5)));
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[ks], st, 0, 0, 0);
       }
       // keep the V operand reads from being hoisted above the S^T products
@@ -205,7 +201,7 @@ __global__ __launch_bounds__(64 * kDqRowWaves * NH, 1) void bwd_dq_kernel(Prefil
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vs + kb * 32 * ROW + roff[ks]);
+        const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vs + kb * 32 * ROW + (roff0 ^ (ks << 5)));
         dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), of[ks], dpt, 0, 0, 0);
       }
       float sv[16];
@@ -225,7 +221,7 @@ __global__ __launch_bounds__(64 * kDqRowWaves * NH, 1) void bwd_dq_kernel(Prefil
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              bw_tr_read(kt, toff[mb][0], toff[mb][1]), sb[h], dqa[mb], 0, 0, 0);
+              bw_tr_read(kt, toff0 ^ bw_tr_xor<D>(mb, 0), toff0 ^ bw_tr_xor<D>(mb, 1)), sb[h], dqa[mb], 0, 0, 0);
       }
     }
   };
