@@ -65,6 +65,30 @@ __device__ __forceinline__ int k_slot(int r, int c) {
 // ... of the V image (transpose reads: 4 consecutive rows x 32 bytes).
 __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r & 3) << 1); }
 
+// O^T += V^T P^T with the accumulator updated in place.  Written out: with
+// the compiler's MFMA the output accumulators, whose old values stay live on
+// the path of a skipped tile, get a second register set and two 64-register
+// copies per kept tile.  Wait states, which the compiler does not see here:
+// the first MFMA of each 16-key step follows vector ALU writes of its B
+// operand (and, on a tile's first, of the rescaled accumulators), which need
+// 2 (s_nop 2 gives 3); the accumulators are next read by vector ALU code after
+// the next tile's score products, or after oacc_drain at the end.
+__device__ __forceinline__ void pv_mfma(f32x16_t& acc, u32x4_t a, bf16x8_t b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void pv_mfma_first(f32x16_t& acc, u32x4_t a, bf16x8_t b) {
+  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// The wait states an MFMA result needs before vector ALU code reads it (the
+// 32x32x16 MFMA: 18), tied to the accumulators so nothing reads them earlier.
+template <int MB>
+__device__ __forceinline__ void oacc_drain(f32x16_t (&o)[MB]) {
+  if constexpr (MB == 4)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]));
+}
+
 template <int D, int NH>
 __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NW = kRowWaves * NH;         // waves in the workgroup
@@ -77,14 +101,13 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   constexpr int LOADS = kTile / ROWS_PER_LOAD / NW;  // per wave per tile (each of K, V)
   static_assert(LOADS >= 1 && LOADS * ROWS_PER_LOAD * NW == kTile, "tile split");
 
-  // Two-stage ring.  Each stage is its own LDS object, and the tile loop is
-  // unrolled by two so every access names its stage at compile time: then the
-  // compiler can tell that reads of one stage do not wait for the
-  // direct-to-LDS loads still filling the other.
-  __shared__ __attribute__((aligned(1024))) unsigned char kst0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char vst0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char kst1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char vst1[TILE_BYTES];
+  // Two-stage ring.  Its loads are direct-to-LDS loads written out in
+  // assembly (dma16), which the compiler does not track: one loop body serves
+  // both stages through a runtime stage base (no duplicated body, no copies of
+  // the accumulators between two register assignments), and the ring waits
+  // for its loads itself (vmcnt 0 before the barrier at the top of a step).
+  __shared__ __attribute__((aligned(1024))) unsigned char kst[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst[2][TILE_BYTES];
   __shared__ float red[NH][kRowWaves];
 
   const int nQ = (a.Lq + kTile - 1) / kTile;
@@ -140,28 +163,43 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   // (base row + l / KCH), physical chunk l % KCH, and fetches the logical
   // chunk that the swizzle puts there.  Rows past Lk read the last key row
   // (their scores are masked to -inf, their P is 0).
-  // Addresses: the tile's first row is a wave-uniform base, the lane's row
-  // within the tile (< 128, clamped to the last key) and chunk a 32-bit offset.
-  auto issue_tile = [&](int j, unsigned char* kdst0, unsigned char* vdst0) {
+  // Addresses: the tile's first row is a wave-uniform base; the lane's offset
+  // within a full tile follows from its offset for load 0 (kgo0, vgo0): load i
+  // covers rows 1024 i / ROW further on, the K swizzle of its rows differs
+  // from load 0's by XOR with chunk bits 2-3 (D = 128: (i & 3) << 2 of the row
+  // bits; D = 64: (i & 1) << 2), and the V swizzle does not change (it sees
+  // r & 3 only).  kgo0 and vgo0 are formed at each issue from the lane index
+  // (a few instructions; held across the tile loop they would not fit in
+  // registers).  Only the last tile clamps rows.
+  auto issue_tile = [&](int j, int st) {
     const int j0 = j * kTile;
-    const int rlast = a.Lk - 1 - j0;  // last valid row of this tile
     const unsigned char* kt = reinterpret_cast<const unsigned char*>(kp) + (size_t)j0 * ROW;
     const unsigned char* vt = reinterpret_cast<const unsigned char*>(vp) + (size_t)j0 * ROW;
-    const int ln = lane_id_fresh();
-    const int lr = ln / KCH, pc = ln % KCH;
+    unsigned char* kd = kst[st] + w * LOADS * ROWS_PER_LOAD * ROW;
+    unsigned char* vd = vst[st] + w * LOADS * ROWS_PER_LOAD * ROW;
+    if (j0 + kTile <= a.Lk) {
+      const int ln = lane_id_fresh();
+      const int lr = ln / KCH, pc = ln % KCH;
+      const int r = w * LOADS * ROWS_PER_LOAD + lr;
+      const unsigned kgo0 = (unsigned)r * ROW + ((unsigned)k_slot<D>(r, pc) << 4);  // an involution
+      const unsigned vgo0 = (unsigned)r * ROW + ((unsigned)(pc ^ ((r & 3) << 1)) << 4);  // v_slot^-1
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r = (w * LOADS + i) * ROWS_PER_LOAD + lr;
-      const unsigned ro = (unsigned)min(r, rlast) * ROW;
-      const unsigned kc = k_slot<D>(r, pc);     // inverse of k_slot (an involution)
-      const unsigned vc = pc ^ ((r & 3) << 1);  // inverse of v_slot
-      const int off = (w * LOADS + i) * ROWS_PER_LOAD * ROW;
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(kt + (ro + (kc << 4))),
-          (void __attribute__((address_space(3)))*)(kdst0 + off), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(vt + (ro + (vc << 4))),
-          (void __attribute__((address_space(3)))*)(vdst0 + off), 16, 0, 0);
+      for (int i = 0; i < LOADS; ++i) {
+        const unsigned ko = (kgo0 ^ (unsigned)((D == 128 ? (i & 3) : (i & 1)) << 6)) + i * 1024u;
+        dma16(kt, ko, kd + i * ROWS_PER_LOAD * ROW);
+        dma16(vt, vgo0 + i * 1024u, vd + i * ROWS_PER_LOAD * ROW);
+      }
+    } else {
+      const int rlast = a.Lk - 1 - j0;  // last valid row of this tile
+      const int ln = lane_id_fresh();
+      const int lr = ln / KCH, pc = ln % KCH;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = (w * LOADS + i) * ROWS_PER_LOAD + lr;
+        const unsigned ro = (unsigned)min(r, rlast) * ROW;
+        dma16(kt, ro + ((unsigned)k_slot<D>(r, pc) << 4), kd + i * ROWS_PER_LOAD * ROW);
+        dma16(vt, ro + ((unsigned)(pc ^ ((r & 3) << 1)) << 4), vd + i * ROWS_PER_LOAD * ROW);
+      }
     }
   };
 
@@ -188,41 +226,48 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   float m2 = neg_inf();              // running max of row rq (log2 units)
   float lpart = 0.f;                 // this lane's half of the row's denominator
 
-  // per-lane LDS offsets (the parts of the addresses that depend on the swizzle)
+  // Per-lane LDS offsets (the parts of the addresses that depend on the
+  // swizzle), formed from the lane index where they are used: held across the
+  // tile loop they would not fit in the registers of two waves per SIMD.
   // K: row kb * 32 + l32, logical chunk 2 ks + g; the swizzle depends on the
-  // row only through l32 (the row block is an immediate offset), so one
-  // offset per k-step.
-  int koff[KS];
-#pragma unroll
-  for (int i = 0; i < KS; ++i) koff[i] = (k_slot<D>(l32, 2 * i + g) << 4) + l32 * ROW;
+  // row only through l32 (the row block is an immediate offset), and k-step
+  // ks's offset is koff(0) ^ (ks << 5) (chunk 2 ks + g differs from chunk g in
+  // bits 1-3 only).
+  auto koff_now = [&]() __attribute__((always_inline)) {
+    const int ln = lane_id_fresh();
+    const int r = ln & 31;
+    return (k_slot<D>(r, ln >> 5) << 4) + r * ROW;
+  };
   // V^T: keys {4g..4g+3} and {8+4g..8+4g+3} of each 16-key step, rows
   // 16 step + 4 g + r16 / 4 (+ 8); columns 32 mb + 16 (lane / 16 & 1) +
   // 4 (r16 & 3).  The swizzle sees only the row's low two bits and chunk bits
-  // 1..2, so two offsets cover every column block.
-  const int r16 = lane & 15;
-  int voff[2];
-  {
-    const int cq = ((lane >> 4) & 1) * 2 + ((r16 & 3) >> 1);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      voff[i] = (v_slot(r16 >> 2, 4 * i + cq) << 4) + (g * 4 + (r16 >> 2)) * ROW + (r16 & 1) * 8;
-  }
+  // 1..2: column blocks 2 m and 2 m + 1 are 128 m bytes on from blocks 0 and
+  // 1, and block 1's offset is block 0's with chunk bit 2 flipped (XOR 64).
+  auto voff_now = [&]() __attribute__((always_inline)) {
+    const int ln = lane_id_fresh();
+    const int q16 = ln & 15, gg = ln >> 5;
+    const int cq = ((ln >> 4) & 1) * 2 + ((q16 & 3) >> 1);
+    return (v_slot(q16 >> 2, cq) << 4) + (gg * 4 + (q16 >> 2)) * ROW + (q16 & 1) * 8;
+  };
 
-  if (plan.count > 0) issue_tile(plan.tile_at(0), kst0, vst0);
+  if (plan.count > 0) issue_tile(plan.tile_at(0), 0);
 
-  // one tile; Ks/Vs: this tile's stage, Kn/Vn: the other stage
-  auto step = [&](int t, const unsigned char* Ks, const unsigned char* Vs, unsigned char* Kn,
-                  unsigned char* Vn) {
+  // one tile, from ring stage t & 1
+  for (int t = 0; t < plan.count; ++t) {
+    const int st = t & 1;
+    const unsigned char* Ks = kst[st];
+    const unsigned char* Vs = vst[st];
     const int j = plan.tile_at(t);
     const int j0 = j * kTile;
     // this tile's loads have landed (own wave), and every wave is past tile t-1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // the stage of tile t-1 is free: start tile t+1
-    if (t + 1 < plan.count) issue_tile(plan.tile_at(t + 1), Kn, Vn);
+    if (t + 1 < plan.count) issue_tile(plan.tile_at(t + 1), st ^ 1);
 
     // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 rows
     f32x16_t sacc[4];
+    const int koff0 = koff_now();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -233,7 +278,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
         u32x4_t kop[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          kop[ks] = *reinterpret_cast<const u32x4_t*>(Ks + kb * 32 * ROW + koff[k4 + ks]);
+          kop[ks] = *reinterpret_cast<const u32x4_t*>(Ks + kb * 32 * ROW + (koff0 ^ ((k4 + ks) << 5)));
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), qf[k4 + ks],
@@ -278,27 +323,30 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     if (mask_writer && lane == 0) mrow[j] = skip ? 1 : 0;
 
     const float m2n = fmaxf(m2, tmax2);
+    // Rescale l and O when some row's running max grew (the factor is exactly
+    // 1 for every other row).  A kept tile can raise m; a skipped one only
+    // when threshold > 1 (with threshold <= 1 a skipped tile lies below every
+    // row's m).  One place for both, so the accumulators keep one register
+    // assignment through the loop.
+    if (__builtin_amdgcn_ballot_w64(m2n != m2) != 0) {
+      // rows that have seen no key yet (m2 = m2n = -inf) take 0, not NaN
+      const float alpha = fast_exp2(m2 - (m2n == neg_inf() ? 0.f : m2n));
+      lpart *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+    }
     if (!skip) {
       const float mref = (m2n == neg_inf()) ? 0.f : m2n;
       // per-row decisions: a row that failed its own test gets P = 0
       const float mexp = (a.per_row && row_skip) ? pos_inf() : mref;
-      // rescale only when some row's running max grew (the factor is exactly
-      // 1 for every other row)
-      if (__builtin_amdgcn_ballot_w64(m2n != m2) != 0) {
-        const float alpha = fast_exp2(m2 - mref);
-        lpart *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
-      }
       // ---- per 32-key block: exponentials, then O^T += V^T P^T (two 16-key
       // steps, V^T operands from transpose reads).
+      const int voff0 = voff_now();
       auto read_v = [&](int kb, int half, u32x4_t (&dst)[MB]) {
         const unsigned char* va = Vs + (kb * 32 + half * 16) * ROW;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int off = (mb >> 1) * 128 + voff[mb & 1];
+          const int off = (mb >> 1) * 128 + (voff0 ^ ((mb & 1) << 6));
           const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + off));
           const s16x4_t hi =
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 8 * ROW + off));
@@ -327,29 +375,17 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
         for (int half = 0; half < 2; ++half) {
           u32x4_t vop[MB];
           read_v(kb, half, vop);
+          pv_mfma_first(oacc[0], vop[0], pb[half]);
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[mb]), pb[half],
-                                                              oacc[mb], 0, 0, 0);
+          for (int mb = 1; mb < MB; ++mb) pv_mfma(oacc[mb], vop[mb], pb[half]);
         }
       }
-    } else if (a.thr_above_1 && m2n > m2) {
-      const float alpha = fast_exp2(m2 - m2n);
-      lpart *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
     }
     m2 = m2n;
-  };
-
-  for (int t = 0; t < plan.count; t += 2) {
-    step(t, kst0, vst0, kst1, vst1);
-    if (t + 1 < plan.count) step(t + 1, kst1, vst1, kst0, vst0);
   }
 
   // ---- epilogue: O / l, lane holds columns 32 mb + 8 (i/4) + 4 g + i%4 of row rq
+  oacc_drain<MB>(oacc);
   const float l = sum_xor32(lpart);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (a.lse && row_ok && g == 0)

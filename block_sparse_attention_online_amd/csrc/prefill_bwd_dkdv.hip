@@ -114,10 +114,15 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
       dva[mb][i] = 0.f;
     }
 
-  // LDS offsets of this lane's row and transpose reads (k-step 0, column
-  // block 0); the others follow by XOR with constants
-  const int roff0 = bw_row_off<D>(lane, 0);
-  const int toff0 = bw_tr_off<D>(lane, 0, 0);
+  // LDS offsets of this lane's row and transpose reads, one register each
+  // (forming them from the first by XOR would cost a VALU instruction per read)
+  int roff[KS], toff[MB][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = bw_row_off<D>(lane, ks);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = bw_tr_off<D>(lane, mb, hi);
 
   const float c2 = a.scale * kLog2e;
 
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
     bf16x8_t tv[2][MB], tq[2][MB];
     f32x4_t l4[4], d4[4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const u32x4_t*>(Qs + (roff0 ^ (ks << 5)));
+    for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const u32x4_t*>(Qs + roff[ks]);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       // ---- stage 1: S for rows 32 rb .. + 32 (accumulator: column = key,
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[ks]), kf[ks], sacc, 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        da[ks] = *reinterpret_cast<const u32x4_t*>(Ds + rb * 32 * ROW + (roff0 ^ (ks << 5)));
+        da[ks] = *reinterpret_cast<const u32x4_t*>(Ds + rb * 32 * ROW + roff[ks]);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         l4[q4] = *reinterpret_cast<const f32x4_t*>(Rs + rb * 32 + 8 * q4 + 4 * g);
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          tv[h][mb] = bw_tr_read(Ds + (rb * 32 + 16 * h) * ROW, toff0 ^ bw_tr_xor<D>(mb, 0), toff0 ^ bw_tr_xor<D>(mb, 1));
+          tv[h][mb] = bw_tr_read(Ds + (rb * 32 + 16 * h) * ROW, toff[mb][0], toff[mb][1]);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         d4[q4] = *reinterpret_cast<const f32x4_t*>(Rs + kTile + rb * 32 + 8 * q4 + 4 * g);
@@ -232,7 +237,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          tq[h][mb] = bw_tr_read(Qs + (rb * 32 + 16 * h) * ROW, toff0 ^ bw_tr_xor<D>(mb, 0), toff0 ^ bw_tr_xor<D>(mb, 1));
+          tq[h][mb] = bw_tr_read(Qs + (rb * 32 + 16 * h) * ROW, toff[mb][0], toff[mb][1]);
 #pragma unroll
       for (int x = 0; x < 2 * MB; ++x) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
       if (rb < 3) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          qa[ks] = *reinterpret_cast<const u32x4_t*>(Qs + (rb + 1) * 32 * ROW + (roff0 ^ (ks << 5)));
+          qa[ks] = *reinterpret_cast<const u32x4_t*>(Qs + (rb + 1) * 32 * ROW + roff[ks]);
       }
 #pragma unroll
       for (int x = 0; x < 2 * MB; ++x) {
