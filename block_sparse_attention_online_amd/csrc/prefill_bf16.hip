@@ -65,30 +65,6 @@ __device__ __forceinline__ int k_slot(int r, int c) {
 // ... of the V image (transpose reads: 4 consecutive rows x 32 bytes).
 __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r & 3) << 1); }
 
-// O^T += V^T P^T with the accumulator updated in place.  Written out: with
-// the compiler's MFMA the output accumulators, whose old values stay live on
-// the path of a skipped tile, get a second register set and two 64-register
-// copies per kept tile.  Wait states, which the compiler does not see here:
-// the first MFMA of each 16-key step follows vector ALU writes of its B
-// operand (and, on a tile's first, of the rescaled accumulators), which need
-// 2 (s_nop 2 gives 3); the accumulators are next read by vector ALU code after
-// the next tile's score products, or after oacc_drain at the end.
-__device__ __forceinline__ void pv_mfma(f32x16_t& acc, u32x4_t a, bf16x8_t b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void pv_mfma_first(f32x16_t& acc, u32x4_t a, bf16x8_t b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-// The wait states an MFMA result needs before vector ALU code reads it (the
-// 32x32x16 MFMA: 18), tied to the accumulators so nothing reads them earlier.
-template <int MB>
-__device__ __forceinline__ void oacc_drain(f32x16_t (&o)[MB]) {
-  if constexpr (MB == 4)
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
-  else
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]));
-}
-
 template <int D, int NH>
 __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NW = kRowWaves * NH;         // waves in the workgroup
@@ -375,9 +351,10 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
         for (int half = 0; half < 2; ++half) {
           u32x4_t vop[MB];
           read_v(kb, half, vop);
-          pv_mfma_first(oacc[0], vop[0], pb[half]);
 #pragma unroll
-          for (int mb = 1; mb < MB; ++mb) pv_mfma(oacc[mb], vop[mb], pb[half]);
+          for (int mb = 0; mb < MB; ++mb)
+            oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[mb]), pb[half],
+                                                              oacc[mb], 0, 0, 0);
         }
       }
     }
@@ -385,7 +362,6 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   }
 
   // ---- epilogue: O / l, lane holds columns 32 mb + 8 (i/4) + 4 g + i%4 of row rq
-  oacc_drain<MB>(oacc);
   const float l = sum_xor32(lpart);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (a.lse && row_ok && g == 0)
