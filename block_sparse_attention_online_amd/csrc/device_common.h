@@ -176,6 +176,63 @@ __device__ __forceinline__ void dma16(const void* gbase, unsigned goff, const un
       : "memory");
 }
 
+// ---- LDS tile swizzle for row and transpose reads --------------------------------
+
+// Physical 16-byte chunk of logical chunk c in row r of a tile image with
+// D bf16 elements per row, for an image read two ways (the backward's Q, dO,
+// K and V; the forward's V), conflict-free for both:
+//  * row reads (MFMA operand with k along the row): one chunk of 16
+//    consecutive rows per LDS cycle, so the XOR term must take 16 different
+//    values over r & 15;
+//  * transpose reads (ds_read_b64_tr_b16, k across rows): 64 bytes (4 chunks)
+//    of 4 consecutive rows per 32 lanes, so those 4 rows must land on 4
+//    different 64-byte bank groups.
+// D = 128: a row is one 256-byte bank line; chunk bits 2-3 take r & 3, bits
+// 0-1 take (r >> 2) & 3.  D = 64: two rows per bank line (r & 1 picks the
+// half); chunk bit 2 takes bit 1 of r, bits 0-1 take (r >> 2) & 3.  Either
+// term is a bijection on r & 15, and XOR with it is its own inverse.
+template <int D>
+__device__ __forceinline__ int dual_slot(int r, int c) {
+  return D == 128 ? c ^ (((r & 3) << 2) | ((r >> 2) & 3))
+                  : c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Per-lane offset of a row read: the A operand of a 32x32x16 MFMA whose rows
+// are tile rows 32 blk + l % 32 and whose k-step ks covers elements
+// 16 ks + 8 (l / 32) .. + 8 of the row.  The swizzle sees r & 15 only, so the
+// 32-row block is an immediate offset (blk * 32 * ROW).
+template <int D>
+__device__ __forceinline__ int dual_row_off(int lane, int ks) {
+  const int l32 = lane & 31, g = lane >> 5;
+  return l32 * 2 * D + (dual_slot<D>(l32, 2 * ks + g) << 4);
+}
+
+// Per-lane offset of a transpose read: the A operand (rows = tile columns
+// 32 mb + l % 32, k = tile rows) of a 16-row k-step, in the row order that the
+// MFMA accumulator layout gives its B operand: lane half g takes rows
+// 4 g .. 4 g + 3 (hi = 0) and 8 + 4 g .. 8 + 4 g + 3 (hi = 1) of the step.
+// Each 16-lane group reads 4 rows x 16 columns (lane: row r16 / 4, columns
+// 4 (r16 % 4) .. + 4 of its 16) and receives one column's 4 rows.
+template <int D>
+__device__ __forceinline__ int dual_tr_off(int lane, int mb, int hi) {
+  const int g = lane >> 5, r16 = lane & 15;
+  const int R = 4 * g + (r16 >> 2) + 8 * hi;
+  const int c = 4 * mb + 2 * ((lane >> 4) & 1) + ((r16 & 3) >> 1);
+  return R * 2 * D + (dual_slot<D>(R, c) << 4) + (r16 & 1) * 8;
+}
+
+// The swizzle is an XOR of chunk bits with row bits, so the offsets of the
+// other k-steps (row reads) and column blocks / halves (transpose reads)
+// follow from the first by XOR with constants: one register per kind.
+//   dual_row_off<D>(l, ks)     == dual_row_off<D>(l, 0) ^ (ks << 5)
+//   dual_tr_off<D>(l, mb, hi)  == dual_tr_off<D>(l, 0, 0) ^ dual_tr_xor<D>(mb, hi)
+template <int D>
+__device__ __forceinline__ constexpr int dual_tr_xor(int mb, int hi) {
+  // hi moves the rows by 8 (bit 11 of the offset for D = 128, bit 10 for
+  // D = 64) and flips bit 1 of the swizzle term ((R >> 2) & 3 gains 2)
+  return (mb << 6) ^ (hi << 5) ^ (hi << (D == 128 ? 11 : 10));
+}
+
 template <class F, int... E>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, E...>) {
   (f(std::integral_constant<int, E>{}), ...);

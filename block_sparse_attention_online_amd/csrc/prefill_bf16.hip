@@ -62,8 +62,6 @@ template <int D>
 __device__ __forceinline__ int k_slot(int r, int c) {
   return D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
 }
-// ... of the V image (transpose reads: 4 consecutive rows x 32 bytes).
-__device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((r & 3) << 1); }
 
 template <int D, int NH>
 __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(PrefillArgs a) {
@@ -141,10 +139,10 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   // (their scores are masked to -inf, their P is 0).
   // Addresses: the tile's first row is a wave-uniform base; the lane's offset
   // within a full tile follows from its offset for load 0 (kgo0, vgo0): load i
-  // covers rows 1024 i / ROW further on, the K swizzle of its rows differs
-  // from load 0's by XOR with chunk bits 2-3 (D = 128: (i & 3) << 2 of the row
-  // bits; D = 64: (i & 1) << 2), and the V swizzle does not change (it sees
-  // r & 3 only).  kgo0 and vgo0 are formed at each issue from the lane index
+  // covers rows 1024 i / ROW further on, and the swizzle of its rows differs
+  // from load 0's by XOR with chunk bits -- K (k_slot): bits 2-3, (i & 3) << 2
+  // for D = 128, (i & 1) << 2 for D = 64; V (dual_slot): bits 0-1, i & 3 for
+  // D = 128, (i & 1) << 1 for D = 64.  kgo0 and vgo0 are formed at each issue from the lane index
   // (a few instructions; held across the tile loop they would not fit in
   // registers).  Only the last tile clamps rows.
   auto issue_tile = [&](int j, int st) {
@@ -158,12 +156,13 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
       const int lr = ln / KCH, pc = ln % KCH;
       const int r = w * LOADS * ROWS_PER_LOAD + lr;
       const unsigned kgo0 = (unsigned)r * ROW + ((unsigned)k_slot<D>(r, pc) << 4);  // an involution
-      const unsigned vgo0 = (unsigned)r * ROW + ((unsigned)(pc ^ ((r & 3) << 1)) << 4);  // v_slot^-1
+      const unsigned vgo0 = (unsigned)r * ROW + ((unsigned)dual_slot<D>(r, pc) << 4);  // likewise
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const unsigned ko = (kgo0 ^ (unsigned)((D == 128 ? (i & 3) : (i & 1)) << 6)) + i * 1024u;
         dma16(kt, ko, kd + i * ROWS_PER_LOAD * ROW);
-        dma16(vt, vgo0 + i * 1024u, vd + i * ROWS_PER_LOAD * ROW);
+        const unsigned vo = (vgo0 ^ (unsigned)(D == 128 ? (i & 3) << 4 : (i & 1) << 5)) + i * 1024u;
+        dma16(vt, vo, vd + i * ROWS_PER_LOAD * ROW);
       }
     } else {
       const int rlast = a.Lk - 1 - j0;  // last valid row of this tile
@@ -174,7 +173,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
         const int r = (w * LOADS + i) * ROWS_PER_LOAD + lr;
         const unsigned ro = (unsigned)min(r, rlast) * ROW;
         dma16(kt, ro + ((unsigned)k_slot<D>(r, pc) << 4), kd + i * ROWS_PER_LOAD * ROW);
-        dma16(vt, ro + ((unsigned)(pc ^ ((r & 3) << 1)) << 4), vd + i * ROWS_PER_LOAD * ROW);
+        dma16(vt, ro + ((unsigned)dual_slot<D>(r, pc) << 4), vd + i * ROWS_PER_LOAD * ROW);
       }
     }
   };
@@ -214,17 +213,10 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     const int r = ln & 31;
     return (k_slot<D>(r, ln >> 5) << 4) + r * ROW;
   };
-  // V^T: keys {4g..4g+3} and {8+4g..8+4g+3} of each 16-key step, rows
-  // 16 step + 4 g + r16 / 4 (+ 8); columns 32 mb + 16 (lane / 16 & 1) +
-  // 4 (r16 & 3).  The swizzle sees only the row's low two bits and chunk bits
-  // 1..2: column blocks 2 m and 2 m + 1 are 128 m bytes on from blocks 0 and
-  // 1, and block 1's offset is block 0's with chunk bit 2 flipped (XOR 64).
-  auto voff_now = [&]() __attribute__((always_inline)) {
-    const int ln = lane_id_fresh();
-    const int q16 = ln & 15, gg = ln >> 5;
-    const int cq = ((ln >> 4) & 1) * 2 + ((q16 & 3) >> 1);
-    return (v_slot(q16 >> 2, cq) << 4) + (gg * 4 + (q16 >> 2)) * ROW + (q16 & 1) * 8;
-  };
+  // V^T: the transpose reads of dual_tr_off (keys {4g..4g+3} and
+  // {8+4g..8+4g+3} of each 16-key step, one value column per lane); the V
+  // image uses dual_slot, which keeps 32 lanes of a transpose read on
+  // different banks (the swizzle it replaced did so for 16 lanes only).
 
   if (plan.count > 0) issue_tile(plan.tile_at(0), 0);
 
@@ -317,15 +309,15 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
       const float mexp = (a.per_row && row_skip) ? pos_inf() : mref;
       // ---- per 32-key block: exponentials, then O^T += V^T P^T (two 16-key
       // steps, V^T operands from transpose reads).
-      const int voff0 = voff_now();
+      const int voff0 = dual_tr_off<D>(lane_id_fresh(), 0, 0);
       auto read_v = [&](int kb, int half, u32x4_t (&dst)[MB]) {
         const unsigned char* va = Vs + (kb * 32 + half * 16) * ROW;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int off = (mb >> 1) * 128 + (voff0 ^ ((mb & 1) << 6));
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + off));
-          const s16x4_t hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 8 * ROW + off));
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(va + (voff0 ^ dual_tr_xor<D>(mb, 0))));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(va + (voff0 ^ dual_tr_xor<D>(mb, 1))));
           const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
           const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
           dst[mb] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};

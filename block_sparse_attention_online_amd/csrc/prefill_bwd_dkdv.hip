@@ -118,11 +118,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
   // (forming them from the first by XOR would cost a VALU instruction per read)
   int roff[KS], toff[MB][2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) roff[ks] = bw_row_off<D>(lane, ks);
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = dual_row_off<D>(lane, ks);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = bw_tr_off<D>(lane, mb, hi);
+    for (int hi = 0; hi < 2; ++hi) toff[mb][hi] = dual_tr_off<D>(lane, mb, hi);
 
   const float c2 = a.scale * kLog2e;
 

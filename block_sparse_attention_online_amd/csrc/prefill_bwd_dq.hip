@@ -153,8 +153,8 @@ __global__ __launch_bounds__(64 * kDqRowWaves * NH, 1) void bwd_dq_kernel(Prefil
 
   // LDS offsets of this lane's row and transpose reads (k-step 0, column
   // block 0); the others follow by XOR with constants
-  const int roff0 = bw_row_off<D>(lane, 0);
-  const int toff0 = bw_tr_off<D>(lane, 0, 0);
+  const int roff0 = dual_row_off<D>(lane, 0);
+  const int toff0 = dual_tr_off<D>(lane, 0, 0);
 
   const float c2 = a.scale * kLog2e;
   const unsigned char* kbase = static_cast<const unsigned char*>(a.k) +
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64 * kDqRowWaves * NH, 1) void bwd_dq_kernel(Prefil
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              bw_tr_read(kt, toff0 ^ bw_tr_xor<D>(mb, 0), toff0 ^ bw_tr_xor<D>(mb, 1)), sb[h], dqa[mb], 0, 0, 0);
+              bw_tr_read(kt, toff0 ^ dual_tr_xor<D>(mb, 0), toff0 ^ dual_tr_xor<D>(mb, 1)), sb[h], dqa[mb], 0, 0, 0);
       }
     }
   };
