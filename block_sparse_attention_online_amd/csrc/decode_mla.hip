@@ -67,12 +67,12 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 // Physical 16-byte chunk = logical chunk ^ swizzle(row).
 //  * 256-byte rows (16 chunks): score reads take one chunk of 16 consecutive
-//    rows -> 16 distinct values; value transpose reads take a 32-byte chunk
-//    pair of 4 consecutive rows -> bits 1..2 distinct, pairs kept together.
+//    rows -> 16 distinct values over r & 15; value transpose reads take
+//    64 bytes (4 chunks) of 4 consecutive rows per 32 lanes -> the 4 rows on
+//    4 different 64-byte bank groups: chunk bits 2-3 take r & 3, bits 0-1
+//    (r >> 2) & 3 (the dual_slot swizzle for D = 128).
 //  * 128-byte rows (8 chunks, two rows per 256 bytes): score reads only.
-__device__ __forceinline__ int swz256(int r) {
-  return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
-}
+__device__ __forceinline__ int swz256(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int swz128(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ unsigned long long tagged(unsigned tag, float x) {
@@ -231,8 +231,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   // ... of the value transpose reads.  Value block vb (columns 32 vb ..),
   // 16-key k-step t, half hi: lane l reads row 16 t + 8 hi + 4 g + (l & 15) / 4,
   // 8 bytes at column 32 vb + 16 ((l >> 4) & 1) + 4 (l & 3).  The swizzle of
-  // that row does not depend on t, and on vb only through an XOR of bits 2..3
-  // of the chunk, so 8 offsets (hi, vb % 4) cover every read.
+  // that row does not depend on t, and vb % 4 enters only through chunk
+  // bits 2..3 (XORed with the row's), so 8 offsets (hi, vb % 4) cover every
+  // read.
   int voff[2][4];
   {
     const int r16 = lane & 15;
