@@ -120,6 +120,8 @@ struct DecodePlan {
   int chain_tiles;     // tiles per chain
   int subs_per_chain;  // sub-splits per chain
   size_t o_off, lse_off, slot_off, timeout_off, bytes;
+  // latent decode with a threshold: kept tiles per sub-split, their share-out
+  size_t kept_off, share_tiles_off, share_count_off, share_mref_off;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -173,7 +175,15 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int Lk, int D, int Dv, bool laten
   p.o_off = 0;
   p.lse_off = align256(rows * (size_t)Dv * sizeof(float));
   p.slot_off = p.lse_off + align256(rows * sizeof(float));
-  p.timeout_off = p.slot_off + align256(slots * (size_t)(Hq / Hkv) * sizeof(unsigned long long));
+  const size_t after_slots =
+      p.slot_off + align256(slots * (size_t)(Hq / Hkv) * sizeof(unsigned long long));
+  p.kept_off = after_slots;
+  p.share_tiles_off = p.kept_off + align256(slots * sizeof(unsigned long long));
+  p.share_count_off = p.share_tiles_off + align256(slots * 64 * sizeof(int));
+  p.share_mref_off = p.share_count_off + align256(slots * sizeof(int));
+  // the timeout counter block stays the last 256 bytes
+  p.timeout_off =
+      latent ? p.share_mref_off + align256((size_t)B * Hq * sizeof(float)) : after_slots;
   p.bytes = p.timeout_off + 256;
   return p;
 }
@@ -412,6 +422,12 @@ int prepare_decode(const ss_decode_params* p, bool stage_partial, ssattn::Decode
   a->part_lse = reinterpret_cast<float*>(ws + pl.lse_off);
   a->lb_slot = reinterpret_cast<unsigned long long*>(ws + pl.slot_off);
   a->lb_timeouts = reinterpret_cast<unsigned int*>(ws + pl.timeout_off);
+  if (k == DecodeKernel::kMla) {
+    a->kept_bits = reinterpret_cast<unsigned long long*>(ws + pl.kept_off);
+    a->share_tiles = reinterpret_cast<int*>(ws + pl.share_tiles_off);
+    a->share_count = reinterpret_cast<int*>(ws + pl.share_count_off);
+    a->share_mref = reinterpret_cast<float*>(ws + pl.share_mref_off);
+  }
   a->B = p->B;
   a->Hq = p->Hq;
   a->Hkv = p->Hkv;

@@ -116,7 +116,9 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16_t& x, f32x16_t& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
 
-template <int NW>
+// SHARE: stage 2 of a thresholded decode (this workgroup's share of the
+// sequence's kept tiles, from the planning launch); otherwise stage 0 or 1.
+template <int NW, bool SHARE>
 __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   constexpr int G = NW * kHeadsPerWave;  // heads per latent head
   constexpr int kThreads = 64 * NW;
@@ -158,7 +160,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   const int head0 = hk * G;                   // first query head of the group
   const int myhead = w * kHeadsPerWave + l32;  // head within the group owned by this lane
 
-  if (T == 0) {  // an empty trailing link: nothing to publish, nobody waits on it
+  // 0: one launch; 1: scores, decisions, kept tiles recorded (no output);
+  // 2: this workgroup's share of the sequence's kept tiles (the output)
+  const int stage = a.mla_stage;
+  if (T == 0 && !SHARE && stage == 1) {  // an empty trailing link: no tile kept, nothing published
+    if (tid == 0) a.kept_bits[(size_t)pair * S + sub] = 0ull;
+    return;
+  }
+  if (T == 0 && !SHARE && stage == 0) {  // an empty trailing link: nothing to publish, nobody waits on it
     for (int idx = tid; idx < G * kDv; idx += kThreads) {
       const size_t rowid = ((size_t)sub * a.B + b) * a.Hq + head0 + idx / kDv;
       a.part_o[rowid * kDv + idx % kDv] = 0.f;
@@ -389,7 +398,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   float mref = neg_inf();  // exponent reference of head myhead (log2 units)
   int nkept = T;
 
-  if (!dense) {
+  if constexpr (SHARE) {
+    // the share the planning launch gave this workgroup
+    const size_t us = (size_t)pair * S + sub;
+    if (tid == 0) s_nsurv = a.share_count[us];
+    if (tid < kTmax) s_surv[tid] = a.share_tiles[us * kTmax + tid];
+    if (tid < G) s_mref[tid] = a.share_mref[(size_t)b * a.Hq + head0 + tid];
+    __syncthreads();
+  } else if (!dense) {
     // ---------------------------------------------------------- 1. score pass
     float tmax = neg_inf();
     pipeline(kStepsPerTile * T, [&](int t) __attribute__((always_inline)) { return t0 + t; },
@@ -414,7 +430,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
     cm = fmaxf(part_red[0][h], part_red[1][h]);
     if (part == 0) {
       s_mref[h] = cm;
-      if (a.subs_per_chain > 1)
+      if (a.subs_per_chain > 1 || stage == 1)
         __hip_atomic_store(&a.lb_slot[lbslot * G + h], tagged(tag, cm), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -473,19 +489,24 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
       const bool kept = valid && !(d < a.log2_thr);
       const unsigned long long bits = __ballot(kept);
       const int idx = __popcll(bits & ((1ull << lane) - 1ull));
-      if (kept) s_surv[idx] = lane;
+      if (kept) s_surv[idx] = t0 + lane;
       if (lane == 0) s_nsurv = __popcll(bits);
+      if (lane == 0 && stage == 1) a.kept_bits[(size_t)pair * S + sub] = bits;
       if (valid && a.mask) a.mask[(size_t)pair * nK + t0 + lane] = kept ? 0 : 1;
     }
     __syncthreads();
+    if (stage == 1) return;  // the planning launch and stage 2 run the kept tiles
+  }
+  if (SHARE || !dense) {
     nkept = s_nsurv;
     mref = s_mref[myhead];
 
     // ---------------------------------------------------------- 3. kept tiles
+    // (s_surv: absolute tile indices)
     if (nkept > 0) {
       const float mr = mref == neg_inf() ? 0.f : mref;
       pipeline(kStepsPerTile * nkept,
-               [&](int t) __attribute__((always_inline)) { return t0 + s_surv[t]; },
+               [&](int t) __attribute__((always_inline)) { return s_surv[t]; },
                [&](const unsigned char* sl, int tile, int st) __attribute__((always_inline)) {
                  f32x16_t s = scores(sl);
                  mask_tail(s, tile * kTile + st * kStepKeys);
@@ -547,6 +568,67 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   if (g == 0) a.part_lse[rowid] = l > 0.f ? (mref + __log2f(l)) * kLn2 : neg_inf();
 }
 
+// Planning launch of a thresholded decode: one workgroup per sequence (batch,
+// latent head).  Its kept tiles, in (sub-split, tile) order, are numbered
+// 0 .. K-1; workgroup o of stage 2 takes ranks [o K / S, (o + 1) K / S)
+// (at most 64, since no sub-split holds more than 64 tiles).  The heads'
+// exponent reference is their max over the whole sequence: the maxima every
+// non-empty sub-split published in stage 1.
+__global__ __launch_bounds__(256) void decode_mla_plan_kernel(DecodeArgs a) {
+  const int S = a.num_splits;
+  const int pair = blockIdx.x;  // b * Hkv + hk
+  const int b = pair / a.Hkv, hk = pair % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int nK = (a.Lk + kTile - 1) / kTile;
+  const int tid = threadIdx.x;
+  __shared__ int s_base[1024];  // exclusive prefix of the kept counts (S <= 1024)
+  __shared__ int s_total;
+  auto first_tile = [&](int s2) {
+    const int c2 = s2 / a.subs_per_chain, k2 = s2 % a.subs_per_chain;
+    return c2 * a.chain_tiles + k2 * a.tiles_per_split;
+  };
+  auto tiles_of = [&](int s2) {
+    const int c2 = s2 / a.subs_per_chain;
+    const int a0 = first_tile(s2);
+    return max(0, min(a0 + a.tiles_per_split, min(c2 * a.chain_tiles + a.chain_tiles, nK)) - a0);
+  };
+  const unsigned long long* bits = a.kept_bits + (size_t)pair * S;
+  for (int h = tid; h < G; h += 256) {
+    float m = neg_inf();
+    for (int s2 = 0; s2 < S; ++s2)
+      if (tiles_of(s2) > 0)
+        m = fmaxf(m, poll_tagged(&a.lb_slot[((size_t)pair * S + s2) * G + h], a.lb_tag,
+                                 a.lb_timeouts));
+    a.share_mref[(size_t)b * a.Hq + hk * G + h] = m;
+  }
+  if (tid == 0) {
+    int run = 0;
+    for (int s2 = 0; s2 < S; ++s2) {
+      s_base[s2] = run;
+      run += __popcll(bits[s2]);
+    }
+    s_total = run;
+  }
+  __syncthreads();
+  const long long K = s_total;
+  for (int o = tid; o < S; o += 256)
+    a.share_count[(size_t)pair * S + o] =
+        (int)(((long long)(o + 1) * K) / S - ((long long)o * K) / S);
+  for (int s2 = tid; s2 < S; s2 += 256) {
+    unsigned long long m = bits[s2];
+    const int a0 = first_tile(s2);
+    long long r = s_base[s2];
+    while (m) {
+      const int t = __builtin_ctzll(m);
+      m &= m - 1ull;
+      const int o = (int)(((r + 1) * S - 1) / K);  // the workgroup whose range holds rank r
+      const int pos = (int)(r - ((long long)o * K) / S);
+      a.share_tiles[((size_t)pair * S + o) * kTmax + pos] = a0 + t;
+      ++r;
+    }
+  }
+}
+
 }  // namespace
 
 bool decode_mla_supported(int D, int Dv, int group, bool latent) {
@@ -557,16 +639,43 @@ int decode_mla_max_tiles(int) { return kTmax; }
 
 int decode_mla_workgroups_per_split(int) { return 1; }
 
-hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const dim3 grid((unsigned)((size_t)a.num_splits * a.B * a.Hkv));
+// Threshold 0: one launch.  Otherwise three on the same stream: stage 1
+// scores every tile and decides (each sub-split publishes its per-head maxima
+// and its kept tiles), the planning launch spreads each sequence's kept tiles
+// evenly over its workgroups, stage 2 runs them.  With chained decisions the
+// first sub-splits of a sequence keep most of their tiles (the running max is
+// still low there), so if each ran its own kept tiles the whole launch would
+// wait on them.
+hipError_t launch_decode_mla(const DecodeArgs& args, hipStream_t s) {
+  const int G = args.Hq / args.Hkv;
+  if (G != 128 && G != 64) return hipErrorInvalidValue;
+  if (args.num_splits > 1024) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((size_t)args.num_splits * args.B * args.Hkv));
+  DecodeArgs a = args;
+  if (a.log2_thr == -__builtin_inff()) {
+    a.mla_stage = 0;
+    if (G == 128)
+      hipLaunchKernelGGL((decode_mla_kernel<4, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_mla_kernel<2, false>), grid, dim3(128), 0, s, a);
+    return hipGetLastError();
+  }
+  a.mla_stage = 1;
   if (G == 128)
-    hipLaunchKernelGGL((decode_mla_kernel<4>), grid, dim3(256), 0, s, a);
-  else if (G == 64)
-    hipLaunchKernelGGL((decode_mla_kernel<2>), grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL((decode_mla_kernel<4, false>), grid, dim3(256), 0, s, a);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_mla_kernel<2, false>), grid, dim3(128), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_mla_plan_kernel, dim3((unsigned)(args.B * args.Hkv)), dim3(256), 0, s,
+                     a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.mla_stage = 2;
+  if (G == 128)
+    hipLaunchKernelGGL((decode_mla_kernel<4, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_mla_kernel<2, true>), grid, dim3(128), 0, s, a);
   return hipGetLastError();
 }
-
 }  // namespace ssattn

@@ -68,6 +68,17 @@ struct DecodeArgs {
   // nothing from a kept tile; row_mask (may be null) is u8 [B, Hq, nK].
   int per_row;
   uint8_t* row_mask;
+  // Latent decode with a threshold: stage 1 scores every tile, decides and
+  // records each sub-split's kept tiles (kept_bits, bit t = its tile t,
+  // [B * Hkv][S]); a planning launch shares each sequence's kept tiles out
+  // evenly (share_tiles [B * Hkv][S][64] absolute tile indices, share_count
+  // [B * Hkv][S], share_mref [B * Hq] the heads' max over the sequence, log2
+  // units); stage 2 runs them.  Stage 0: one launch (threshold 0).
+  int mla_stage;
+  unsigned long long* kept_bits;
+  int* share_tiles;
+  int* share_count;
+  float* share_mref;
 };
 
 // Arguments of the backward launches of a bf16 prefill.

@@ -164,12 +164,16 @@ def test_workspace_bytes(ss):
     assert n >= 3 * 4 * 128 * 4
     for args in [(16, 32, 8, 32768, 128, 128, 0), (2, 8, 2, 1000, 64, 64, 99)]:
         assert ss.ss_attn_decode_workspace_bytes(*args) > 0
-    # latent decode: split outputs, lse, per-row maxima
+    # latent decode: split outputs, lse, per-row maxima, the timeout block,
+    # then the share-out of a thresholded decode: kept-tile masks (8 B per
+    # sub-split), 64 tile indices and a count per sub-split, each head's max
     S = 32  # B8 Hq128 Lk16384: 32 sub-splits of 4 tiles
     o = S * 8 * 128 * 512 * 4
     lse = S * 8 * 128 * 4
     slots = S * 8 * 128 * 8
-    assert ss.ss_attn_decode_workspace_bytes(8, 128, 1, 16384, 576, 512, 0) == o + lse + slots + 256
+    share = 2048 + S * 8 * 64 * 4 + 1024 + 8 * 128 * 4
+    assert ss.ss_attn_decode_workspace_bytes(8, 128, 1, 16384, 576, 512, 0) == (
+        o + lse + slots + 256 + share)
 
 
 # --------------------------------------------------------------------------- argument checks
