@@ -49,7 +49,9 @@ METRIC = "prefill TFLOP/s + decode KV GB/s at ~70% tile skip; speedup vs dense"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gqa_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_online_amd", "csrc", "decode_gqa.hip")
+# the decode kernel's device code: its source and the device helpers it includes
+KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_online_amd", "csrc", f)
+               for f in ("decode_gqa.hip", "device_common.h")]
 
 
 def log(*a):
@@ -57,8 +59,11 @@ def log(*a):
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # --------------------------------------------------------------------------- decode
