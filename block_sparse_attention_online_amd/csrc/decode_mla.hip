@@ -313,7 +313,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
     for (int i = 0; i < 16; ++i) oacc[vb][i] = 0.f;
   float lpart = 0.f;  // this lane's share of the head's denominator
 
-  // p = exp2(s c - mref) from raw scores s, lpart += p, then O^T += V^T P^T
+  // p = exp2(s c - mref) from raw scores s, lpart += bf16(p), then O^T += V^T P^T
   // over the step's keys
   auto accumulate = [&](const f32x16_t& s, float mref, const unsigned char* sl)
                         __attribute__((always_inline)) {
@@ -343,8 +343,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
       for (int e = 0; e < 4; ++e) {
         const float p0 = fast_exp2(fmaf(s[8 * t + 2 * e], c, -mref));
         const float p1 = fast_exp2(fmaf(s[8 * t + 2 * e + 1], c, -mref));
-        lpart += p0 + p1;
         pw[e] = pack_bf16x2(p0, p1);
+        lpart = add_bf16x2(pw[e], lpart);
       }
       pb[t] = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
     }

@@ -39,6 +39,15 @@ __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned int, r);
 }
 
+// acc + lo + hi of a packed bf16 pair, one v_dot2c_f32_bf16 against (1, 1): a
+// row sum of probabilities taken from the very bf16 values the P*V product
+// uses, at half the vector instructions of two fp32 adds.
+__device__ __forceinline__ float add_bf16x2(unsigned int w, float acc) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, acc, false);
+}
+
 // 2^x on the hardware exponential unit.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
