@@ -593,21 +593,63 @@ __global__ __launch_bounds__(256) void decode_mla_plan_kernel(DecodeArgs a) {
     return max(0, min(a0 + a.tiles_per_split, min(c2 * a.chain_tiles + a.chain_tiles, nK)) - a0);
   };
   const unsigned long long* bits = a.kept_bits + (size_t)pair * S;
-  for (int h = tid; h < G; h += 256) {
+  // Stage 1 has finished before this launch, so every non-empty sub-split's
+  // published maxima and kept tiles are in memory: plain loads, all issued
+  // together, no polling.  A value without this launch's tag where a
+  // sub-split had tiles would be a lost publish; it is counted with the
+  // look-back timeouts and left out of the max.
+  __shared__ float s_part[256];
+  {
+    const int per = 256 / G;  // threads per head
+    const int h = tid % G;
     float m = neg_inf();
-    for (int s2 = 0; s2 < S; ++s2)
-      if (tiles_of(s2) > 0)
-        m = fmaxf(m, poll_tagged(&a.lb_slot[((size_t)pair * S + s2) * G + h], a.lb_tag,
-                                 a.lb_timeouts));
-    a.share_mref[(size_t)b * a.Hq + hk * G + h] = m;
-  }
-  if (tid == 0) {
-    int run = 0;
-    for (int s2 = 0; s2 < S; ++s2) {
-      s_base[s2] = run;
-      run += __popcll(bits[s2]);
+    unsigned bad = 0;
+#pragma unroll 4
+    for (int s2 = tid / G; s2 < S; s2 += per) {
+      const unsigned long long v = a.lb_slot[((size_t)pair * S + s2) * G + h];
+      const bool use = tiles_of(s2) > 0;
+      const bool fresh = (unsigned)(v >> 32) == a.lb_tag;
+      m = use && fresh ? fmaxf(m, __uint_as_float((unsigned)v)) : m;
+      bad += use && !fresh;
     }
-    s_total = run;
+    if (bad) atomicAdd(a.lb_timeouts, bad);
+    s_part[tid] = m;
+  }
+  // kept counts: thread t holds sub-splits 4t .. 4t+3; exclusive scan over
+  // the 256 threads' sums in LDS
+  __shared__ int s_scan[2][256];
+  int cnt[4], own = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s2 = 4 * tid + i;
+    const unsigned long long w = bits[min(s2, S - 1)];  // loaded unconditionally
+    cnt[i] = s2 < S ? __popcll(w) : 0;
+    own += cnt[i];
+  }
+  s_scan[0][tid] = own;
+  __syncthreads();
+  if (tid < G) {
+    float m = s_part[tid];
+    for (int p2 = 1; p2 < 256 / G; ++p2) m = fmaxf(m, s_part[p2 * G + tid]);
+    a.share_mref[(size_t)b * a.Hq + hk * G + tid] = m;
+  }
+  int src = 0;
+#pragma unroll
+  for (int d = 1; d < 256; d <<= 1) {
+    const int v = s_scan[src][tid] + (tid >= d ? s_scan[src][tid - d] : 0);
+    s_scan[src ^ 1][tid] = v;
+    src ^= 1;
+    __syncthreads();
+  }
+  {
+    int run = s_scan[src][tid] - own;  // exclusive
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s2 = 4 * tid + i;
+      if (s2 < S) s_base[s2] = run;
+      run += cnt[i];
+    }
+    if (tid == 255) s_total = s_scan[src][255];
   }
   __syncthreads();
   const long long K = s_total;
