@@ -11,7 +11,10 @@
 // One workgroup per (batch, query head).  The split weights are formed once
 // (all lse values loaded at the same time, a workgroup max, the exponentials)
 // and kept in LDS; then every thread sums its value columns over the splits
-// with independent loads.
+// with independent loads.  When each thread owns one value column and there
+// are at most 32 splits, the column's partials are loaded into registers
+// before the weights are formed, so the whole merge waits on memory about
+// once instead of once per few splits.
 
 #include "device_common.h"
 #include "launch.h"
@@ -21,6 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxSplitsInLds = 4096;
+constexpr int kRegSplits = 32;  // splits whose partials one thread holds in registers
 
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float wsplit[kMaxSplitsInLds];
@@ -30,6 +34,17 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) 
   const size_t rows = (size_t)a.B * a.Hq;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
+
+  // fast path: one column per thread, partials loaded ahead of the weights
+  const bool in_regs = a.Dv <= kThreads && S <= kRegSplits;
+  const size_t step = rows * a.Dv;
+  float ov[kRegSplits];
+  if (in_regs) {
+    const float* po = a.part_o + (size_t)bh * a.Dv + (tid < a.Dv ? tid : 0);
+#pragma unroll
+    for (int s = 0; s < kRegSplits; ++s)  // past S: the last split again, not used
+      ov[s] = po[(size_t)(s < S ? s : S - 1) * step];
+  }
 
   float mx = neg_inf();
   for (int s = tid; s < S; s += kThreads) {
@@ -56,10 +71,21 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) 
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 
   unsigned short* op = static_cast<unsigned short*>(a.out) + (size_t)bh * a.Dv;
+  if (in_regs) {
+    if (tid < a.Dv) {
+      float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+      for (int s = 0; s < kRegSplits; s += 2) {
+        if (s < S) o0 = fmaf(wsplit[s], ov[s], o0);
+        if (s + 1 < S) o1 = fmaf(wsplit[s + 1], ov[s + 1], o1);
+      }
+      op[tid] = (unsigned short)(pack_bf16x2((o0 + o1) * inv, 0.f) & 0xffffu);
+    }
+    return;
+  }
   for (int dv = tid; dv < a.Dv; dv += kThreads) {
     float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
     const float* po = a.part_o + (size_t)bh * a.Dv + dv;
-    const size_t step = rows * a.Dv;
     const int Sl = S < kMaxSplitsInLds ? S : kMaxSplitsInLds;
     int s = 0;
     for (; s + 4 <= Sl; s += 4) {
