@@ -599,12 +599,17 @@ __global__ __launch_bounds__(256) void decode_mla_plan_kernel(DecodeArgs a) {
   // sub-split had tiles would be a lost publish; it is counted with the
   // look-back timeouts and left out of the max.
   __shared__ float s_part[256];
+  // this thread's kept masks first (sub-splits 4t .. 4t+3; past S the last
+  // again, not used), so their loads overlap those of the maxima
+  unsigned long long kw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kw[i] = bits[min(4 * tid + i, S - 1)];
   {
     const int per = 256 / G;  // threads per head
     const int h = tid % G;
     float m = neg_inf();
     unsigned bad = 0;
-#pragma unroll 4
+#pragma unroll 16
     for (int s2 = tid / G; s2 < S; s2 += per) {
       const unsigned long long v = a.lb_slot[((size_t)pair * S + s2) * G + h];
       const bool use = tiles_of(s2) > 0;
@@ -618,13 +623,14 @@ __global__ __launch_bounds__(256) void decode_mla_plan_kernel(DecodeArgs a) {
   // kept counts: thread t holds sub-splits 4t .. 4t+3; exclusive scan over
   // the 256 threads' sums in LDS
   __shared__ int s_scan[2][256];
+  __shared__ unsigned long long s_bits[1024];
   int cnt[4], own = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s2 = 4 * tid + i;
-    const unsigned long long w = bits[min(s2, S - 1)];  // loaded unconditionally
-    cnt[i] = s2 < S ? __popcll(w) : 0;
+    cnt[i] = s2 < S ? __popcll(kw[i]) : 0;
     own += cnt[i];
+    if (s2 < S) s_bits[s2] = kw[i];
   }
   s_scan[0][tid] = own;
   __syncthreads();
@@ -652,22 +658,20 @@ __global__ __launch_bounds__(256) void decode_mla_plan_kernel(DecodeArgs a) {
     if (tid == 255) s_total = s_scan[src][255];
   }
   __syncthreads();
-  const long long K = s_total;
+  // Products of a rank or a count with S stay below 64 S^2 <= 2^26: 32-bit.
+  const int K = s_total;
   for (int o = tid; o < S; o += 256)
-    a.share_count[(size_t)pair * S + o] =
-        (int)(((long long)(o + 1) * K) / S - ((long long)o * K) / S);
-  for (int s2 = tid; s2 < S; s2 += 256) {
-    unsigned long long m = bits[s2];
-    const int a0 = first_tile(s2);
-    long long r = s_base[s2];
-    while (m) {
-      const int t = __builtin_ctzll(m);
-      m &= m - 1ull;
-      const int o = (int)(((r + 1) * S - 1) / K);  // the workgroup whose range holds rank r
-      const int pos = (int)(r - ((long long)o * K) / S);
-      a.share_tiles[((size_t)pair * S + o) * kTmax + pos] = a0 + t;
-      ++r;
-    }
+    a.share_count[(size_t)pair * S + o] = ((o + 1) * K) / S - (o * K) / S;
+  // one thread per (sub-split, tile) position: a kept tile's rank is its
+  // sub-split's base plus the kept tiles before it in the mask
+  for (int g = tid; g < S * kTmax; g += 256) {
+    const int s2 = g / kTmax, t = g % kTmax;
+    const unsigned long long m = s_bits[s2];
+    if (!((m >> t) & 1ull)) continue;
+    const int r = s_base[s2] + __popcll(m & ((1ull << t) - 1ull));
+    const int o = ((r + 1) * S - 1) / K;  // the workgroup whose range holds rank r
+    const int pos = r - (o * K) / S;
+    a.share_tiles[((size_t)pair * S + o) * kTmax + pos] = first_tile(s2) + t;
   }
 }
 
