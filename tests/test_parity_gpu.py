@@ -276,6 +276,18 @@ def test_decode_mla_16k_full_size(ss, thr, mode):
                  name=w.name, mode=mode)
 
 
+def test_decode_mla_128k_full_size(ss):
+    """Latent decode at the 131072-key size the latent timing uses (B8 Hq128),
+    chained splits, at a threshold near its 70 % skip point, so the share-out
+    of kept tiles over each sequence's workgroups runs at its real shape; the
+    oracle checks one sampled sequence."""
+    w = WORKLOADS["mla_decode_128k"]
+    x = make_inputs(w)
+    _, mask = check_decode(ss, x, w.scale, 0.9866, 0, pairs=[(5, 0)], latent_dv=512,
+                           name=w.name, mode="chained")
+    assert 0.6 < float((mask[5, 0] == 1).mean()) < 0.8
+
+
 # --------------------------------------------------------------------------- determinism
 
 def test_repeat_runs_are_bitwise_identical(ss):
