@@ -56,6 +56,17 @@ def test_library_exports_every_declared_symbol(ss):
         assert hasattr(ss.lib(), n)
 
 
+def test_missing_library_fails_loudly(ss, monkeypatch, tmp_path):
+    """Without the built library every entry point raises; there is no
+    fallback that would compute anything elsewhere."""
+    monkeypatch.setattr(ss, "_LIB", None)
+    monkeypatch.setattr(ss, "library_path", lambda: str(tmp_path / "libssattn.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        ss.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        ss.ss_version()
+
+
 def test_version(ss):
     assert "gfx950" in ss.ss_version()
 
