@@ -51,6 +51,7 @@ constexpr int kDqk = 576;                 // latent key width
 constexpr int kDv = 512;                  // value width (leading columns of the key row)
 constexpr int kHeadsPerWave = 32;
 constexpr int kTmax = 64;                 // tiles per sub-split
+constexpr int kShareMinTiles = 16;        // tiles per sub-split from which the kept tiles are shared out
 constexpr int kStepKeys = 32;             // keys per ring step
 constexpr int kStepsPerTile = kTile / kStepKeys;
 constexpr int kBlkBytes = kStepKeys * 256;               // [32 keys x 128 columns] bf16
@@ -685,10 +686,11 @@ int decode_mla_max_tiles(int) { return kTmax; }
 
 int decode_mla_workgroups_per_split(int) { return 1; }
 
-// Threshold 0: one launch.  Otherwise three on the same stream: stage 1
-// scores every tile and decides (each sub-split publishes its per-head maxima
-// and its kept tiles), the planning launch spreads each sequence's kept tiles
-// evenly over its workgroups, stage 2 runs them.  With chained decisions the
+// Threshold 0, or few tiles per sub-split: one launch.  Otherwise three on
+// the same stream: stage 1 scores every tile and decides (each sub-split
+// publishes its per-head maxima and its kept tiles), the planning launch
+// spreads each sequence's kept tiles evenly over its workgroups, stage 2 runs
+// them.  With chained decisions the
 // first sub-splits of a sequence keep most of their tiles (the running max is
 // still low there), so if each ran its own kept tiles the whole launch would
 // wait on them.
@@ -698,7 +700,16 @@ hipError_t launch_decode_mla(const DecodeArgs& args, hipStream_t s) {
   if (args.num_splits > 1024) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((size_t)args.num_splits * args.B * args.Hkv));
   DecodeArgs a = args;
-  if (a.log2_thr == -__builtin_inff()) {
+  // The share-out pays where a sub-split holds many tiles: chained decisions
+  // then leave the first sub-splits of a sequence with most of theirs and
+  // the rest with few.  With few tiles per sub-split that imbalance is small
+  // and the two extra launches and the second pass's start-up cost more than
+  // they save; one launch then scores, decides and runs each sub-split's own
+  // kept tiles (on 8 sequences of 16K / 32K keys, 4 / 8 tiles per
+  // sub-split: 100 / 150 us in one launch, 121 / 164 us shared out; of
+  // 64K / 128K keys, 16 / 32 tiles: 256 / 456 us against 229 / 365 us).
+  const bool share = a.tiles_per_split >= kShareMinTiles;
+  if (a.log2_thr == -__builtin_inff() || !share) {
     a.mla_stage = 0;
     if (G == 128)
       hipLaunchKernelGGL((decode_mla_kernel<4, false>), grid, dim3(256), 0, s, a);

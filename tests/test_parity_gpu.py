@@ -253,6 +253,8 @@ MLA_CASES = [
     ("mla128_one_key", 1, 128, 1, 1, 3.0, 0.1),
     ("mla128_many_splits", 1, 128, 2500, 99, 9.0, 0.05),
     ("mla128_long_chain", 1, 128, 20000, 0, 9.0, 0.02),
+    ("mla128_share_out", 2, 128, 8192, 2, 9.0, 0.05),  # 32 tiles per sub-split: shared out
+    ("mla64_share_out_ragged", 1, 64, 9000, 3, 9.0, 0.05),
 ]
 
 
