@@ -134,3 +134,76 @@ def test_backward_pins_catch_planted_mistake(name, monkeypatch):
 def test_unmutated_backward_battery_passes():
     for check in backward_battery():
         check()
+
+
+# --------------------------------------------------------------------------- grader
+
+import oracle.grading as grading  # noqa: E402
+from tests import test_grading_pins as gpins  # noqa: E402
+
+GRADING_MUTATIONS = {
+    "far-flip term dropped": ('"ok": bool(far_diff.sum() == 0 and agree >= MIN_AGREEMENT)',
+                              '"ok": bool(agree >= MIN_AGREEMENT)'),
+    "agreement bound dropped": ('"ok": bool(far_diff.sum() == 0 and agree >= MIN_AGREEMENT)',
+                                '"ok": bool(far_diff.sum() == 0)'),
+    "statistic read in log2 units": ("r = np.exp(d) / thr", "r = np.exp2(d) / thr"),
+    "margin inverted": ("near = np.abs(r - 1.0) <= NEAR_REL", "near = np.abs(r - 1.0) > NEAR_REL"),
+    "absolute instead of relative margin": ("near = np.abs(r - 1.0) <= NEAR_REL",
+                                            "near = np.abs(np.exp(d) - thr) <= NEAR_REL"),
+    "selection ignored": ("diff = (g != r) & sel", "diff = (g != r)"),
+    "zero threshold makes every tile near": ("    if thr <= 0:\n        return np.zeros(d.shape, bool)\n",
+                                             "    if thr <= 0:\n        return np.ones(d.shape, bool)\n"),
+    "relative error against the wrong operand": (
+        "return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))",
+        "return float(np.linalg.norm(a - b) / max(np.linalg.norm(a), 1e-300))"),
+    "row bound takes the mean": ("return float(e.max()) if e.size else 0.0",
+                                 "return float(e.mean()) if e.size else 0.0"),
+    "row errors over columns": ("return np.linalg.norm(a2 - b2, axis=1) / np.maximum(nb, floor)",
+                                "return np.linalg.norm(a2 - b2) / np.maximum(nb, floor)"),
+}
+
+
+def grading_mutant(old, new):
+    with open(grading.__file__) as f:
+        src = f.read()
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("grading_mutant")
+    exec(compile(src.replace(old, new), "grading_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def grading_battery():
+    for name in dir(gpins):
+        fn = getattr(gpins, name)
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        if name == "test_near_band_is_relative_one_in_a_thousand_in_natural_log_units":
+            for thr in (1e-4, 0.01, 0.7105, 1.0, 3.0):
+                yield lambda fn=fn, thr=thr: fn(thr)
+        elif name == "test_near_flips_above_one_in_a_thousand_fail":
+            for flips, ok in ((10, True), (11, False), (20, False)):
+                yield lambda fn=fn, flips=flips, ok=ok: fn(flips, ok)
+        else:
+            yield fn
+
+
+@pytest.mark.parametrize("name", sorted(GRADING_MUTATIONS))
+def test_grading_pins_catch_planted_mistake(name, monkeypatch):
+    mod = grading_mutant(*GRADING_MUTATIONS[name])
+    for e in ("near_threshold", "grade_masks", "rel_l2", "row_rel_l2", "max_row_rel_l2"):
+        monkeypatch.setattr(grading, e, getattr(mod, e))
+    caught = []
+    for check in grading_battery():
+        try:
+            check()
+        except (AssertionError, ValueError):
+            caught.append(check)
+    assert caught, f"no grader pin caught the planted mistake: {name}"
+
+
+def test_unmutated_grading_battery_passes():
+    n = 0
+    for check in grading_battery():
+        check()
+        n += 1
+    assert n >= 15

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.grading import grade_masks, rel_l2
+from oracle.grading import ROW_FACTOR, grade_masks, max_row_rel_l2, rel_l2
 from synth import paged_decode
 
 pytestmark = pytest.mark.gpu
@@ -80,6 +80,8 @@ def check_paged(ss, x, scale, name, factor=0.0, thresholds=None, num_splits=0):
         forced = oracle.decode(qb, kb, vb, scale, thr, 1, force_mask=mb)
         err = rel_l2(out[b:b + 1], forced["out"])
         assert err <= 1e-2, f"{name}: sequence {b} (L={L}, thr={thr:.3g}) rel-L2 {err}"
+        row = max_row_rel_l2(out[b:b + 1], forced["out"])
+        assert row <= ROW_FACTOR * 1e-2, f"{name}: sequence {b} worst row rel-L2 {row}"
         skipped += int((mb == 1).sum())
         visited += mb.size
     log(f"[paged {name}] lengths={lens} skip={skipped / max(visited, 1):.3f}")

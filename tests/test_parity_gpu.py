@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.grading import grade_masks, rel_l2
+from oracle.grading import ROW_FACTOR, grade_masks, max_row_rel_l2, rel_l2
 from synth import WORKLOADS, clustered_decode, clustered_prefill, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -70,12 +70,15 @@ def check_prefill(ss, x, scale, causal, thr, order, dtype, blocks=None, name="")
                             force_mask=np.where(sel_mask if sel_mask is not None else True, mask, 0),
                             blocks=blocks)
     err = rel_l2(out[sel_rows], forced["out"][sel_rows])
+    row = max_row_rel_l2(out[sel_rows], forced["out"][sel_rows])
     own = rel_l2(out[sel_rows], ref["out"][sel_rows])
     visited = np.isin(mask, (0, 1)) if sel_mask is None else (np.isin(mask, (0, 1)) & sel_mask)
     skip = float((mask[visited] == 1).mean()) if visited.any() else 0.0
     log(f"[prefill {name}] thr={thr} order={order} skip={skip:.3f} rel-L2 vs forced={err:.2e} "
-        f"vs oracle mask={own:.2e} mask agreement={gr['agreement']:.4f} near={gr['near']}")
+        f"vs oracle mask={own:.2e} worst row={row:.2e} mask agreement={gr['agreement']:.4f} "
+        f"near={gr['near']}")
     assert err <= TOL[dtype], f"{name}: rel-L2 {err}"
+    assert row <= ROW_FACTOR * TOL[dtype], f"{name}: worst row rel-L2 {row}"
     assert np.isfinite(out[sel_rows]).all()
     return out, mask
 
@@ -119,6 +122,7 @@ def test_prefill_tiny_f32_workload(ss, thr):
     gr = grade_masks(mask.cpu().numpy(), ref["mask"], ref["delta"], thr)
     assert gr["ok"], gr
     err = rel_l2(out.cpu().numpy(), ref["out"])
+    assert max_row_rel_l2(out.cpu().numpy(), ref["out"]) <= ROW_FACTOR * 1e-5
     dense = oracle.dense_prefill(x["q"], x["k"], x["v"], w.scale, False)
     log(f"[tiny_f32] thr={thr} skip={ref['skip_fraction']:.3f} rel-L2={err:.2e} "
         f"vs dense={rel_l2(out.cpu().numpy(), dense):.2e}")
@@ -201,11 +205,14 @@ def check_decode(ss, x, scale, thr, S, pairs=None, latent_dv=None, name="", mode
     forced = oracle.decode(x["q"], x["k"], x["v"], scale, thr, S_ref, latent_dv=latent_dv,
                            pairs=pairs, force_mask=mask)
     err = rel_l2(out[sel_rows], forced["out"][sel_rows])
+    row = max_row_rel_l2(out[sel_rows], forced["out"][sel_rows])
     own = rel_l2(out[sel_rows], ref["out"][sel_rows])
     sm = mask if sel_mask is None else mask[sel_mask]
     log(f"[decode {name}] mode={mode} thr={thr} splits={S} skip={float((sm == 1).mean()):.3f} "
-        f"rel-L2 vs forced={err:.2e} vs oracle mask={own:.2e} agreement={gr['agreement']:.4f}")
+        f"rel-L2 vs forced={err:.2e} vs oracle mask={own:.2e} worst row={row:.2e} "
+        f"agreement={gr['agreement']:.4f}")
     assert err <= TOL["bf16"], f"{name}: rel-L2 {err}"
+    assert row <= ROW_FACTOR * TOL["bf16"], f"{name}: worst row rel-L2 {row}"
     return out, mask
 
 

@@ -26,7 +26,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.grading import grade_masks, rel_l2
+from oracle.grading import ROW_FACTOR, grade_masks, max_row_rel_l2, rel_l2
 from synth import WORKLOADS, clustered_decode, clustered_prefill, make_inputs
 from tests.test_parity_gpu import TOL, log
 
@@ -101,6 +101,8 @@ def check_prefill_rows(ss, x, scale, causal, thr, order, dtype, name, blocks=Non
         f"{float((tmask[vis_t] == 1).mean()) if vis_t.any() else 0.0:.3f} rel-L2 vs forced="
         f"{err:.2e} agreement={gr['agreement']:.4f} near={gr['near']}")
     assert err <= TOL[dtype], f"{name}: rel-L2 {err}"
+    row = max_row_rel_l2(out[sel_rows], forced["out"][sel_rows])
+    assert row <= ROW_FACTOR * TOL[dtype], f"{name}: worst row rel-L2 {row}"
     assert np.isfinite(out[sel_rows]).all()
 
 
@@ -187,6 +189,8 @@ def check_decode_rows(ss, x, scale, thr, S, mode, name, pairs=None):
         f"{float((rmask[sel] == 1).mean()):.3f} tile skip={float((tmask == 1).mean()):.3f} "
         f"rel-L2 vs forced={err:.2e} agreement={gr['agreement']:.4f}")
     assert err <= TOL["bf16"], f"{name}: rel-L2 {err}"
+    row = max_row_rel_l2(out[sel_rows], forced["out"][sel_rows])
+    assert row <= ROW_FACTOR * TOL["bf16"], f"{name}: worst row rel-L2 {row}"
 
 
 DECODE_ROW_CASES = [
