@@ -13,6 +13,13 @@ exp(tile_max - running_max) < threshold with everything else fixed), so a
 bisection in log(threshold) on the kernel's own skip mask finds the threshold
 for a target; (a, b) then come from a least-squares line through
 ln(threshold * L) = ln a + b * s over measured (threshold, L, s) points.
+
+A fitted line may ask for more than the test can mean: above a threshold of
+1 the test exp(tile_max - running_max) < threshold no longer bounds a skipped
+key's softmax weight (it passes tiles whose maximum exceeds the running
+max), so a calibrated threshold is clamped to 1 and the target reported as
+not reachable there, exactly as bisection reports a target that even a
+threshold of 1 does not reach.
 """
 
 from __future__ import annotations
@@ -58,9 +65,26 @@ def bisect_threshold(run, target: float, lo: float = 1e-8, hi: float = 1.0,
     return best[0], best[1], True
 
 
+def calibrated_threshold(a: float, b: float, target: float, seqlen: int, *,
+                         timestep=None, disabled_until=None) -> tuple:
+    """(threshold, reachable) for the calibrated factor a*exp(b*target) / seqlen
+    as the library resolves it (timestep gating included: 0 when gated off),
+    clamped to at most 1.  ``reachable`` is False when the fit asked for a
+    threshold above 1."""
+    from . import ss_resolve_threshold
+
+    thr = ss_resolve_threshold("calibrated", a=a, b=b, target_sparsity=target, seqlen=seqlen,
+                               timestep=timestep, disabled_until=disabled_until)
+    if thr > 1.0:
+        return 1.0, False
+    return thr, True
+
+
 def fit_factor(points) -> tuple:
     """Least-squares (a, b) of ln(threshold * L) = ln a + b * s over
-    ``points`` = [(threshold, L, s), ...].  With a single distinct s, b = 0."""
+    ``points`` = [(threshold, L, s), ...].  With a single distinct s, b = 0.
+    The line is not bounded: use calibrated_threshold to turn it into a
+    threshold a kernel call may take."""
     xs = [p[2] for p in points]
     ys = [math.log(p[0] * p[1]) for p in points]
     n = len(points)

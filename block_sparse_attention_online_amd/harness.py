@@ -34,9 +34,12 @@ sections "The threshold" and "Timestep gating"; BLASST summary page, section
 "Calibratie en Thresholding" (threshold = a / L with a fitted so the
 sparsity stays fixed across context lengths).
 
-Every timed call is preceded by a rewrite of a 1 GiB buffer, so no call
-finds its K/V in L2 or in the 256 MB last-level cache; times are the median
-of the per-call HIP event times on the current stream.  Each run prints one
+Every timed call is preceded by a read of a 1 GiB buffer, so no call finds
+its K/V in L2 or in the 256 MB last-level cache (a read, not a rewrite: a
+rewrite leaves dirty lines whose write-back would land in the timed call);
+times are the median of the per-call HIP event times on the current stream.
+Calibrated thresholds are clamped to 1 (calibrate.calibrated_threshold); a
+target that needs more is reported with reachable = false.  Each run prints one
 JSON object per measured point; --out also writes a markdown table.
 """
 
@@ -55,7 +58,7 @@ import torch
 from . import (lib, mask_shape_decode, mask_shape_prefill, ss_attn_decode_partial,
                ss_attn_decode_combine, ss_attn_decode_workspace_bytes, ss_attn_prefill_ex,
                ss_decode_num_splits, ss_resolve_threshold)
-from .calibrate import bisect_threshold, fit_factor, skip_fraction
+from .calibrate import bisect_threshold, calibrated_threshold, fit_factor, skip_fraction
 
 BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
@@ -223,25 +226,25 @@ def run_video(args):
         if not math.isfinite(a):
             continue
         for tgt in (0.5, 0.7, 0.9):
-            thr = ss_resolve_threshold("calibrated", a=a, b=b, target_sparsity=tgt, seqlen=L)
+            thr, reach = calibrated_threshold(a, b, tgt, L)
             ms = timer.ms(lambda: run(thr), iters=9)
             fl = prefill_flops(mask.cpu().numpy(), w.D, w.Dv)
             emit({"workload": w.name, "replicate": 0, "stage": "calibrated", "order": order,
-                  "target": tgt, "threshold": float(f"{thr:.6g}"),
+                  "target": tgt, "threshold": float(f"{thr:.6g}"), "reachable": reach,
                   "skip": round(skip_fraction(mask), 4), "ms": round(ms, 3),
                   "tflops_executed": round(fl / ms / 1e9, 1),
                   "frac_bf16_peak": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
                   "speedup": round(dense_ms / ms, 3),
                   "rel_l2_vs_dense": float(f"{rel_l2_gpu(out, dense_out):.3e}")}, rows)
         for t in (1.0, 0.6, 0.2):
-            thr = ss_resolve_threshold("calibrated", a=a, b=b, target_sparsity=0.7, seqlen=L,
-                                       timestep=t, disabled_until=0.7)
+            thr, reach = calibrated_threshold(a, b, 0.7, L, timestep=t, disabled_until=0.7)
             ms = timer.ms(lambda: run(thr), iters=9)
             emit({"workload": w.name, "replicate": 0, "stage": "gating", "order": order,
                   "timestep": t, "disabled_until": 0.7, "mode": "dense" if thr == 0 else "sparse",
-                  "threshold": float(f"{thr:.6g}"), "skip": round(skip_fraction(mask), 4),
-                  "ms": round(ms, 3)}, rows)
-    cols = ["replicate", "stage", "order", "threshold", "a", "b", "target", "timestep", "mode",
+                  "threshold": float(f"{thr:.6g}"), "reachable": reach,
+                  "skip": round(skip_fraction(mask), 4), "ms": round(ms, 3)}, rows)
+    cols = ["replicate", "stage", "order", "threshold", "reachable", "a", "b", "target",
+            "timestep", "mode",
             "skip", "ms", "tflops_executed", "frac_bf16_peak", "fa_tflops", "speedup",
             "rel_l2_vs_dense"]
     return rows, cols
@@ -299,14 +302,13 @@ def run_latent(args):
             kbytes = w.B * w.Lk * 576 * 2
             dense_ms = timer.ms(lambda: call(0.0))
             dense_out = out.clone()
-            cases = [("bisected", per_ctx[n][0])]
+            cases = [("bisected", per_ctx[n][0], per_ctx[n][2])]
             if math.isfinite(a):
-                cases.append(("calibrated", ss_resolve_threshold(
-                    "calibrated", a=a, b=b, target_sparsity=0.7, seqlen=w.Lk)))
+                cases.append(("calibrated",) + calibrated_threshold(a, b, 0.7, w.Lk))
             emit({"workload": f"mla_decode_{n}k", "r": r, "stage": "dense",
                   "ms": round(dense_ms, 4), "k_gbs": round(kbytes / dense_ms / 1e6, 1),
                   "frac_hbm": round(kbytes / dense_ms / 1e6 / HBM_PEAK_GBS, 4)}, rows)
-            for kind, thr in cases:
+            for kind, thr, reach in cases:
                 ms = timer.ms(lambda: call(thr))
                 s = skip_at(thr)
                 call(thr)
@@ -318,7 +320,7 @@ def run_latent(args):
                 flops = 2.0 * w.Hq * (w.B * w.Lk * 576 + kept_keys * 512)
                 emit({"workload": f"mla_decode_{n}k", "r": r, "stage": kind,
                       "threshold": float(f"{thr:.6g}"),
-                      "reachable": per_ctx[n][2] if kind == "bisected" else None,
+                      "reachable": reach,
                       "skip": round(s, 4), "ms": round(ms, 4),
                       "k_gbs": round(kbytes / ms / 1e6, 1),
                       "frac_hbm": round(kbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
@@ -518,25 +520,27 @@ def run_stability(args):
                   "skip": round(s32, 4), "reachable": reach}, rows)
             for L in ctxs:
                 B, call, skip_at = data[L]
-                thr_a = ss_resolve_threshold("direct", threshold=factor / L, seqlen=L)
+                thr_a = ss_resolve_threshold("direct", threshold=min(factor / L, 1.0), seqlen=L)
+                clamped = factor / L > 1.0
                 s_fixed = skip_at(t32)
                 s_scaled = skip_at(thr_a)
                 dense_ms = timer.ms(lambda: call(0.0), iters=7)
                 ms = timer.ms(lambda: call(thr_a), iters=7)
-                closed = (round(gumbel_closed_form_skip(L, factor), 4) if dist == "gumbel"
+                closed = (round(gumbel_closed_form_skip(L, thr_a * L), 4) if dist == "gumbel"
                           else None)
                 emit({"keys": dist, "target": tgt, "L": L, "B": B,
                       "skip_fixed_threshold": round(s_fixed, 4),
                       "skip_factor_over_L": round(s_scaled, 4),
                       "closed_form_factor_over_L": closed,
                       "threshold_factor_over_L": float(f"{thr_a:.6g}"),
+                      "factor_over_L_clamped_to_1": clamped,
                       "dense_ms": round(dense_ms, 4), "ms": round(ms, 4),
                       "speedup": round(dense_ms / ms, 3)}, rows)
         del data
         torch.cuda.empty_cache()
     cols = ["keys", "target", "stage", "L", "B", "threshold", "factor", "skip", "reachable",
             "skip_fixed_threshold", "skip_factor_over_L", "closed_form_factor_over_L",
-            "threshold_factor_over_L", "dense_ms", "ms", "speedup"]
+            "threshold_factor_over_L", "factor_over_L_clamped_to_1", "dense_ms", "ms", "speedup"]
     return rows, cols
 
 

@@ -109,6 +109,23 @@ def test_resolve_threshold(ss):
                                    disabled_until=0.7) == 0.0
 
 
+def test_calibrated_threshold_is_clamped_to_one(ss):
+    """Above 1 the test no longer bounds a skipped key's weight: a fitted
+    factor that asks for more is clamped and reported as not reachable."""
+    from block_sparse_attention_online_amd.calibrate import calibrated_threshold
+
+    thr, ok = calibrated_threshold(3.0, 2.0, 0.7, 32760)
+    assert ok and thr == pytest.approx(3.0 * math.exp(1.4) / 32760, rel=1e-7)
+    thr, ok = calibrated_threshold(3.0, 2.0, 0.7, 20)        # 3 e^1.4 / 20 = 0.608
+    assert ok and thr == pytest.approx(3.0 * math.exp(1.4) / 20, rel=1e-7)
+    thr, ok = calibrated_threshold(3.0, 2.0, 0.7, 12)        # 1.014 asked for
+    assert (thr, ok) == (1.0, False)
+    thr, ok = calibrated_threshold(5e5, 1.0, 0.9, 32760)
+    assert (thr, ok) == (1.0, False)
+    # gated off: dense, whatever the fit
+    assert calibrated_threshold(5e5, 1.0, 0.9, 32760, timestep=1.0, disabled_until=0.7) == (0.0, True)
+
+
 @pytest.mark.parametrize("kw", [dict(mode="calibrated", a=1.0, b=1.0, target_sparsity=1.5),
                                 dict(mode="calibrated", a=float("nan"), b=1.0),
                                 dict(mode="calibrated", a=-1.0, b=0.0),
