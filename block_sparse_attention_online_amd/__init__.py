@@ -24,6 +24,7 @@ __all__ = [
     "SSError", "TILE", "ORDERS", "mask_shape_prefill", "mask_shape_decode",
     "ss_attn_decode_paged", "GRANULARITIES", "row_mask_shape_prefill", "row_mask_shape_decode",
     "ss_attn_prefill_backward", "ss_attn_prefill_backward_workspace_bytes",
+    "ss_attn_decode_lookback_timeouts",
 ]
 
 TILE = 128
@@ -111,6 +112,8 @@ _SIGNATURES = {
     "ss_attn_decode_paged": (_I, [ctypes.POINTER(_DecodePagedParams), _P]),
     "ss_attn_decode_partial": (_I, [ctypes.POINTER(_DecodeParams), _P]),
     "ss_attn_decode_combine": (_I, [ctypes.POINTER(_DecodeParams), _P]),
+    "ss_attn_decode_lookback_timeouts": (_I, [ctypes.POINTER(_DecodeParams),
+                                              ctypes.POINTER(ctypes.c_uint), _I, _P]),
     "ss_attn_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "ss_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "ss_factor": (_I, [_I, _D, _D, _D, _D, _I64, ctypes.POINTER(_D)]),
@@ -334,7 +337,7 @@ def ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits=0) -> int:
 
 
 def _decode_params(q, k, v, out, dv, scale, threshold, num_splits, split_mode, skip_mask,
-                   workspace, granularity="tile", row_mask=None):
+                   workspace, granularity="tile", row_mask=None, alloc_workspace=True):
     if q.dim() != 3 or k.dim() != 4:
         raise ValueError("q must be [B, Hq, D] and k [B, Hkv, Lk, D]")
     B, Hq, D = q.shape
@@ -359,17 +362,18 @@ def _decode_params(q, k, v, out, dv, scale, threshold, num_splits, split_mode, s
         mptr = _dev(skip_mask, "skip_mask", torch.uint8)
     if split_mode not in SPLIT_MODES:
         raise ValueError(f"split_mode must be one of {sorted(SPLIT_MODES)}")
-    if workspace is None:
+    if workspace is None and alloc_workspace:  # zeroed: the give-up counter starts at 0
         need = ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, num_splits)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     gran, rptr = _granularity(granularity, row_mask, row_mask_shape_decode(B, Hq, Lk))
     p = _DecodeParams(_dev(q, "q", dt), _dev(k, "k", dt), vptr,
                       None if out is None else _dev(out, "out", dt), B, Hq, Hkv, Lk, D, Dv,
                       float(scale), float(threshold), int(num_splits), SPLIT_MODES[split_mode],
-                      mptr, _dev(workspace, "workspace"),
-                      workspace.numel() * workspace.element_size(), gran, rptr)
+                      mptr, None if workspace is None else _dev(workspace, "workspace"),
+                      0 if workspace is None else workspace.numel() * workspace.element_size(),
+                      gran, rptr)
     return p, workspace, (B, Hq, Dv)
 
 
@@ -390,6 +394,20 @@ def ss_attn_decode_combine(q, k, workspace, out, *, v=None, dv=None, num_splits=
     p, _, _ = _decode_params(q, k, v, out, dv, 1.0, 0.0, num_splits, split_mode, None, workspace)
     _check(lib().ss_attn_decode_combine(ctypes.byref(p), _stream(stream, out.device)))
     return out
+
+
+def ss_attn_decode_lookback_timeouts(q, k, workspace, *, v=None, dv=None, num_splits=0,
+                                     split_mode="chained", reset=False, stream=None) -> int:
+    """Look-back waits that gave up, counted in ``workspace`` by the decode
+    calls that used it (cumulative; ``reset=True`` clears it after reading).
+    ``q``, ``k`` (and ``v`` or ``dv``), ``num_splits`` and ``split_mode`` must
+    be those of the calls; only their sizes are used.  Synchronizes the
+    stream."""
+    p, _, _ = _decode_params(q, k, v, None, dv, 1.0, 0.0, num_splits, split_mode, None, workspace)
+    n = ctypes.c_uint()
+    _check(lib().ss_attn_decode_lookback_timeouts(ctypes.byref(p), ctypes.byref(n), int(bool(reset)),
+                                                  _stream(stream, q.device)))
+    return int(n.value)
 
 
 def ss_attn_decode_ex(q, k, v=None, out=None, *, dv=None, scale=None, threshold=0.0,

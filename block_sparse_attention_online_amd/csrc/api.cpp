@@ -546,6 +546,26 @@ int ss_attn_decode_paged(const ss_decode_paged_params* p, hipStream_t stream) {
   return ok();
 }
 
+int ss_attn_decode_lookback_timeouts(const ss_decode_params* p, unsigned int* count_out,
+                                     int reset, hipStream_t stream) {
+  if (!count_out) return fail(SS_ERR_INVALID_ARG, "count_out is null");
+  ssattn::DecodeArgs a{};
+  DecodeKernel k;
+  if (int rc = prepare_decode(p, false, &a, &k)) return rc;
+  unsigned int v = 0;
+  hipError_t e = hipMemcpyAsync(&v, a.lb_timeouts, sizeof(v), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "reading the look-back counter");
+  if (reset) {
+    static const unsigned int zero = 0;
+    e = hipMemcpyAsync(a.lb_timeouts, &zero, sizeof(zero), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "clearing the look-back counter");
+  }
+  *count_out = v;
+  return ok();
+}
+
 int ss_attn_decode_ex(const ss_decode_params* p, hipStream_t stream) {
   if (!p) return fail(SS_ERR_INVALID_ARG, "params is null");
   if (!p->out) return fail(SS_ERR_INVALID_ARG, "out must be non-null");

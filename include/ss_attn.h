@@ -269,6 +269,29 @@ int ss_attn_decode_ex(const ss_decode_params* p, hipStream_t stream);
 int ss_attn_decode_partial(const ss_decode_params* p, hipStream_t stream);
 int ss_attn_decode_combine(const ss_decode_params* p, hipStream_t stream);
 
+/* Look-back give-ups of chained splits.  A chained split waits for the
+ * running maxima that the earlier splits of its sequence publish.  Those
+ * splits are dispatched earlier -- the hardware starts workgroups in order of
+ * their index, which forward progress relies on -- so the wait is short; it
+ * is still bounded (about 2^21 polls), and a wait that gives up decides
+ * without that split's maxima (it keeps tiles the exact rule might skip: the
+ * output stays a valid softmax over the kept keys, but the mask can differ
+ * from the oracle's) and adds 1 to a 32-bit counter in the last 256 bytes of
+ * the workspace.  The counter is cumulative over the calls that use one
+ * workspace and starts at whatever the workspace held: zero the workspace
+ * once when allocating it, or call this with reset = 1 before the calls to
+ * be checked.
+ *
+ * Reads the counter into *count_out after the work already queued on
+ * `stream` (it synchronizes the stream, so do not call it under graph
+ * capture) and, with reset != 0, sets it back to 0.  p locates the counter
+ * exactly as the decode call does: pass the fields of that call (sizes,
+ * num_splits, split_mode, workspace, workspace_bytes; q, k, v, out and the
+ * masks are not read).  For ss_attn_decode_paged pass Lk = max_seq_len and
+ * a non-null v. */
+int ss_attn_decode_lookback_timeouts(const ss_decode_params* p, unsigned int* count_out,
+                                     int reset, hipStream_t stream);
+
 /*
  * Decode over a block-paged KV cache, one query token per sequence, sequences
  * of different lengths, each with its own threshold (design page "The

@@ -378,3 +378,16 @@ def test_paged_decode_rejects_before_launch(ss, over, code):
     assert paged_call(ss, **over) == code
     assert ss.ss_last_error()
 
+
+
+def test_lookback_query_rejects_bad_arguments(ss):
+    p = ss._DecodeParams(FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 1000, 128, 128, 0.1, 0.01, 0, 0, None,
+                         FAKE, 1 << 30, 0, None)
+    assert ss.lib().ss_attn_decode_lookback_timeouts(ctypes.byref(p), None, 0, None) == -1
+    n = ctypes.c_uint()
+    p.workspace = None
+    assert ss.lib().ss_attn_decode_lookback_timeouts(ctypes.byref(p), ctypes.byref(n), 0,
+                                                     None) == -4
+    p.workspace, p.Hq = FAKE, 7
+    assert ss.lib().ss_attn_decode_lookback_timeouts(ctypes.byref(p), ctypes.byref(n), 0,
+                                                     None) == -1
