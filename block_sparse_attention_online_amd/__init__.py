@@ -24,10 +24,11 @@ __all__ = [
     "SSError", "TILE", "ORDERS", "mask_shape_prefill", "mask_shape_decode",
     "ss_attn_decode_paged", "GRANULARITIES", "row_mask_shape_prefill", "row_mask_shape_decode",
     "ss_attn_prefill_backward", "ss_attn_prefill_backward_workspace_bytes",
-    "ss_attn_decode_lookback_timeouts",
+    "ss_attn_decode_lookback_timeouts", "ss_attn_decode_noalloc", "DECODE_NOALLOC_SCRATCH_BYTES",
 ]
 
 TILE = 128
+DECODE_NOALLOC_SCRATCH_BYTES = 48 << 20  # SS_DECODE_NOALLOC_SCRATCH_BYTES in ss_attn.h
 ORDERS = {"ascending": 0, "diag_first": 1}
 SS_FACTOR_DIRECT, SS_FACTOR_CALIBRATED = 0, 1
 _DTYPE = {torch.bfloat16: 0, torch.float32: 1}
@@ -112,6 +113,7 @@ _SIGNATURES = {
     "ss_attn_decode_paged": (_I, [ctypes.POINTER(_DecodePagedParams), _P]),
     "ss_attn_decode_partial": (_I, [ctypes.POINTER(_DecodeParams), _P]),
     "ss_attn_decode_combine": (_I, [ctypes.POINTER(_DecodeParams), _P]),
+    "ss_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _P, _P]),
     "ss_attn_decode_lookback_timeouts": (_I, [ctypes.POINTER(_DecodeParams),
                                               ctypes.POINTER(ctypes.c_uint), _I, _P]),
     "ss_attn_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
@@ -393,6 +395,23 @@ def ss_attn_decode_combine(q, k, workspace, out, *, v=None, dv=None, num_splits=
     ``q``, ``k`` (and ``v`` or ``dv``) only give the sizes; they are not read."""
     p, _, _ = _decode_params(q, k, v, out, dv, 1.0, 0.0, num_splits, split_mode, None, workspace)
     _check(lib().ss_attn_decode_combine(ctypes.byref(p), _stream(stream, out.device)))
+    return out
+
+
+def ss_attn_decode_noalloc(q, k, v=None, out=None, *, dv=None, scale=None, threshold=0.0,
+                           num_splits=0, skip_mask=None, stream=None):
+    """ss_attn_decode (chained splits) with the split workspace taken from the
+    library's fixed per-GPU array (DECODE_NOALLOC_SCRATCH_BYTES): the library
+    allocates nothing.  ``out`` is allocated here only when None.  Calls that
+    overlap in time on one GPU race (they share the array)."""
+    if out is None:
+        Dv = int(dv) if v is None else v.shape[3]
+        out = torch.empty((q.shape[0], q.shape[1], Dv), dtype=torch.bfloat16, device=q.device)
+    p, _, _ = _decode_params(q, k, v, out, dv, scale, threshold, num_splits, "chained",
+                             skip_mask, None, alloc_workspace=False)
+    _check(lib().ss_attn_decode_noalloc(p.q, p.k, p.v, p.out, p.B, p.Hq, p.Hkv, p.Lk, p.D, p.Dv,
+                                        p.scale, p.threshold, p.num_splits, p.skip_mask_out,
+                                        _stream(stream, q.device)))
     return out
 
 

@@ -244,6 +244,10 @@ int validate_prefill(const ss_prefill_params* p) {
 
 }  // namespace
 
+namespace ssattn {
+int report_error(int code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace ssattn
+
 extern "C" {
 
 const char* ss_last_error(void) { return g_err; }
@@ -448,6 +452,14 @@ int prepare_decode(const ss_decode_params* p, bool stage_partial, ssattn::Decode
 }
 
 }  // namespace
+
+namespace ssattn {
+int validate_decode(const ss_decode_params* p) {
+  DecodeArgs a{};
+  DecodeKernel k;
+  return prepare_decode(p, true, &a, &k);
+}
+}  // namespace ssattn
 
 extern "C" {
 

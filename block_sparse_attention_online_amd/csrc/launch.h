@@ -99,6 +99,17 @@ struct PrefillBwdArgs {
   int causal;
 };
 
+// Sets the thread-local message ss_last_error() returns; returns code.
+int report_error(int code, const char* msg);
+}  // namespace ssattn
+
+#include "ss_attn.h"
+
+namespace ssattn {
+// Every host-side check of a decode call (the split stage's), workspace size
+// included; touches no device and launches nothing.
+int validate_decode(const ss_decode_params* p);
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 bool prefill_bf16_supported(int D, int Dv);

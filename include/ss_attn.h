@@ -293,6 +293,33 @@ int ss_attn_decode_lookback_timeouts(const ss_decode_params* p, unsigned int* co
                                      int reset, hipStream_t stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, hosts that forbid it):
+ * ss_attn_decode without the workspace arguments.  The split workspace is a
+ * fixed array of SS_DECODE_NOALLOC_SCRATCH_BYTES inside this library, one per
+ * GPU, held from the library's first use on that GPU until the process ends;
+ * this call allocates nothing and frees nothing.
+ *
+ * Arguments, layouts, splits and results are those of ss_attn_decode
+ * (CHAINED splits).  With num_splits = 0 the automatic count is lowered, if
+ * needed, to the largest one whose workspace fits the array (chained
+ * decisions do not depend on the count).  A call whose workspace does not
+ * fit even so -- or an explicit num_splits whose workspace does not fit --
+ * returns SS_ERR_WORKSPACE without launching.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or different host threads, without ordering
+ * between them) race and give wrong results.  Calls on one stream are
+ * ordered and safe.  The look-back give-up counter of this array is not
+ * exposed.
+ */
+#define SS_DECODE_NOALLOC_SCRATCH_BYTES (48u << 20)
+
+int ss_attn_decode_noalloc(const void* q, const void* k, const void* v, void* out, int B,
+                           int Hq, int Hkv, int Lk, int D, int Dv, float scale, float threshold,
+                           int num_splits, uint8_t* skip_mask_out, hipStream_t stream);
+
+/*
  * Decode over a block-paged KV cache, one query token per sequence, sequences
  * of different lengths, each with its own threshold (design page "The
  * threshold": the threshold is a factor over the sequence length, so every

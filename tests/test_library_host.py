@@ -380,6 +380,49 @@ def test_paged_decode_rejects_before_launch(ss, over, code):
 
 
 
+def noalloc_call(ss, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, Lk=1000, D=128, Dv=128,
+             scale=0.1, thr=0.01, S=0, mask=None)
+    a.update(over)
+    return ss.lib().ss_attn_decode_noalloc(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"],
+                                           a["Hkv"], a["Lk"], a["D"], a["Dv"], a["scale"],
+                                           a["thr"], a["S"], a["mask"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(Lk=0), -1), (dict(Hq=7), -1),
+    (dict(S=-1), -1), (dict(thr=-1.0), -1), (dict(scale=float("nan")), -1),
+    (dict(Hq=48, Hkv=2), -2), (dict(D=96, Dv=96), -2),
+    # an explicit split count whose workspace (2^15 splits x 16 x 32 rows x 129
+    # floats ~ 8.7 GB) exceeds the fixed array
+    (dict(B=16, Hq=32, Hkv=8, Lk=1 << 22, S=1 << 15), -4),
+])
+def test_noalloc_decode_rejects_before_touching_a_device(ss, over, code):
+    assert noalloc_call(ss, **over) == code
+    msg = ss.ss_last_error()
+    assert msg
+    if code == -4:
+        assert "allocation-free" in msg and str(ss.DECODE_NOALLOC_SCRATCH_BYTES) in msg
+
+
+def test_noalloc_scratch_size_matches_header(ss):
+    src = open(HEADER).read()
+    m = re.search(r"#define SS_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == ss.DECODE_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_fits_the_measured_decode_workloads(ss):
+    # GQA decode, Llama-3.1-8B shape at 32K keys: the automatic split count fits
+    assert ss.ss_attn_decode_workspace_bytes(16, 32, 8, 32768, 128, 128, 0) <= \
+        ss.DECODE_NOALLOC_SCRATCH_BYTES
+    # latent decode, 8 sequences x 128 heads: the automatic count needs more,
+    # a lower count fits (the entry point lowers it by itself)
+    assert ss.ss_attn_decode_workspace_bytes(8, 128, 1, 131072, 576, 512, 0) > \
+        ss.DECODE_NOALLOC_SCRATCH_BYTES
+    assert ss.ss_attn_decode_workspace_bytes(8, 128, 1, 131072, 576, 512, 16) <= \
+        ss.DECODE_NOALLOC_SCRATCH_BYTES
+
+
 def test_lookback_query_rejects_bad_arguments(ss):
     p = ss._DecodeParams(FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 1000, 128, 128, 0.1, 0.01, 0, 0, None,
                          FAKE, 1 << 30, 0, None)
