@@ -22,10 +22,18 @@ timed with HIP events on the stream they run on, and ``value`` uses the mean
 of those step times.  ``warm_value`` is the same decode run back to back
 (wall clock over the steps, caches left as the previous step left them).
 
-``roofline`` is for the decode kernel alone; ``cpu_baseline`` times the fp64
-CPU oracle on a bounded sample of the same decode.  ``latent`` is the
-latent-cache decode (B8, 128 heads, 576-wide rows, 131072 keys);
-``backward`` the skip-aware backward of the causal GQA prefill.
+``roofline`` is for the decode kernel alone: its algorithmic bytes (K, the V
+of kept tiles, q) over its mean event time; the split partials it writes are
+reported beside them, not counted.  ``rel_l2_vs_dense`` of every leg is the
+output's relative L2 distance from the same kernels at threshold 0.  Every
+chained decode checks that no look-back wait gave up.  ``decode_wide_gap`` is
+the same decode on keys with a wide score gap (r = 9), where ~70 % skip comes
+at a small threshold and a small error.  ``cpu_baseline`` times the fp64 CPU
+oracle on a bounded sample of the same decode.  ``video`` is the non-causal
+video-DiT attention (B1 H24, 32760 tokens) at the calibrated threshold of
+target 0.7 and under timestep gating; ``latent`` the latent-cache decode
+(B8, 128 heads, 576-wide rows, 131072 keys); ``backward`` the skip-aware
+backward of the causal GQA prefill.
 
 Usage: python bench.py [--steps K] [--warmup W] [--target-skip 0.7]
        python bench.py --copy-probe       (a plain 1 GiB device copy, for
@@ -86,18 +94,26 @@ def decode_bytes(mask_np, B, Hq, Hkv, Lk, D, Dv, S):
             "partials": part_bytes, "v_dense": B * Hkv * Lk * Dv * 2}
 
 
-def bench_decode(ss, torch, args):
+def rel_l2(torch, a, b) -> float:
+    a, b = a.float(), b.float()
+    return float(torch.linalg.norm(a - b) / torch.linalg.norm(b))
+
+
+def bench_decode(ss, torch, args, r=None):
     from block_sparse_attention_online_amd.calibrate import bisect_threshold, skip_fraction
     from synth import WORKLOADS, make_inputs
 
     w = WORKLOADS["gqa_decode_32k"]
+    if r is not None:
+        w = w.replace(r=r)
     t = time.time()
     x = make_inputs(w)
     log(f"[decode] generated {w.name} in {time.time() - t:.1f}s")
     q, k, v = (x[n].cuda() for n in "qkv")
     B, Hq, Hkv, Lk, D, Dv = w.B, w.Hq, w.Hkv, w.Lk, w.D, w.Dv
     S = ss.ss_decode_num_splits(B, Hq, Hkv, Lk, D, Dv)
-    ws = torch.empty(ss.ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, 0),
+    # zeroed once: its last 256 bytes count look-back waits that gave up
+    ws = torch.zeros(ss.ss_attn_decode_workspace_bytes(B, Hq, Hkv, Lk, D, Dv, 0),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device="cuda")
     mask = torch.empty(ss.mask_shape_decode(B, Hkv, Lk), dtype=torch.uint8, device="cuda")
@@ -114,11 +130,12 @@ def bench_decode(ss, torch, args):
         torch.cuda.synchronize()
         return skip_fraction(mask)
 
-    if args.threshold is not None:
-        thr, reachable = args.threshold, True
+    fixed = args.threshold if r is None else args.wide_threshold
+    if fixed is not None:
+        thr, reachable = fixed, True
     else:
         thr, _, reachable = bisect_threshold(skip_at, args.target_skip)
-    log(f"[decode] threshold {thr:.6g} (reachable={reachable}) splits={S}")
+    log(f"[decode r={w.r:g}] threshold {thr:.6g} (reachable={reachable}) splits={S}")
 
     def timed(th, steps, warmup):
         """(step ms, decode kernel ms, combine ms) over `steps` cold steps, each
@@ -150,16 +167,25 @@ def bench_decode(ss, torch, args):
     res = {"workload": w, "S": S, "thr": thr, "reachable": reachable, "x": x}
     if not args.only_sparse_decode:
         res["dense"] = timed(0.0, args.steps, args.warmup)
-        log(f"[decode] dense: step {res['dense'][0]:.4f} ms, kernel {res['dense'][1]:.4f} ms, "
-            f"warm step {res['dense'][3]:.4f} ms")
+        dense_out = out.clone()
+        log(f"[decode r={w.r:g}] dense: step {res['dense'][0]:.4f} ms, kernel "
+            f"{res['dense'][1]:.4f} ms, warm step {res['dense'][3]:.4f} ms")
     res["sparse"] = timed(thr, args.steps, args.warmup)
     torch.cuda.synchronize()
+    # every chained split of every call since the workspace was zeroed (the
+    # bisection's, the dense and the sparse timed ones) found its
+    # predecessors' maxima
+    res["lookback_timeouts"] = ss.ss_attn_decode_lookback_timeouts(q, k, ws, v=v)
+    assert res["lookback_timeouts"] == 0, \
+        f"{res['lookback_timeouts']} look-back waits gave up: decisions not those of one pass"
+    if not args.only_sparse_decode:
+        res["rel_l2_vs_dense"] = rel_l2(torch, out, dense_out)
     res["mask"] = mask.cpu().numpy()
     res["skip"] = skip_fraction(mask)
     res["bytes"] = decode_bytes(res["mask"], B, Hq, Hkv, Lk, D, Dv, S)
-    log(f"[decode] sparse: step {res['sparse'][0]:.4f} ms, kernel {res['sparse'][1]:.4f} ms, "
-        f"combine {res['sparse'][2]:.4f} ms, warm step {res['sparse'][3]:.4f} ms, "
-        f"skip {res['skip']:.3f}")
+    log(f"[decode r={w.r:g}] sparse: step {res['sparse'][0]:.4f} ms, kernel "
+        f"{res['sparse'][1]:.4f} ms, combine {res['sparse'][2]:.4f} ms, warm step "
+        f"{res['sparse'][3]:.4f} ms, skip {res['skip']:.3f}")
     return res
 
 
@@ -214,7 +240,9 @@ def bench_prefill(ss, torch, args, r, order):
         return ms, mask.cpu().numpy()
 
     dense_ms, dmask = timed(0.0)
+    dense_out = out.clone()
     sparse_ms, smask = timed(thr)
+    err = rel_l2(torch, out, dense_out)
     fl_d, vis, _ = prefill_flops(dmask, w.D, w.Dv)
     fl_s, _, kept = prefill_flops(smask, w.D, w.Dv)
     fa = 4.0 * w.B * w.Hq * w.Lq * w.Lk * w.D * 0.5
@@ -226,8 +254,103 @@ def bench_prefill(ss, torch, args, r, order):
            "tflops_executed": round(fl_s / sparse_ms / 1e9, 2),
            "dense_tflops_executed": round(fl_d / dense_ms / 1e9, 2),
            "frac_of_bf16_peak": round(fl_s / sparse_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
-           "fa_convention_tflops": round(fa / sparse_ms / 1e9, 2)}
+           "dense_frac_of_bf16_peak": round(fl_d / dense_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+           "fa_convention_tflops": round(fa / sparse_ms / 1e9, 2),
+           "rel_l2_vs_dense": float(f"{err:.3e}")}
     log(f"[prefill r={r} {order}] {res}")
+    return res
+
+
+# --------------------------------------------------------------------------- video DiT
+
+def bench_video(ss, torch, args):
+    """Non-causal video-DiT self-attention (B1 H24, 13x42x60 = 32760 latent
+    tokens, D128, smooth-field generator).  Per visit order, the calibrated
+    factor a*exp(b*s) is fitted on replicate 1 (a sweep of thresholds, least
+    squares of ln(threshold*L) = ln a + b*s over the points with 2-98 % skip);
+    replicate 0 is then timed dense, at the calibrated threshold of target
+    0.7 (clamped to 1), and under timestep gating (dense until t <= 0.7) at
+    t = 1.0 (dense) and t = 0.6 (sparse)."""
+    import numpy as np
+
+    from block_sparse_attention_online_amd.calibrate import (calibrated_threshold, fit_factor,
+                                                             skip_fraction)
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS["video_dit_32760"]
+    L = w.Lk
+    grid = [float(f"{t:.3g}") for t in np.logspace(-6, 0, 13)]
+    mask = torch.empty(ss.mask_shape_prefill(w.B, w.Hq, w.Lq, w.Lk), dtype=torch.uint8,
+                       device="cuda")
+
+    def load(seed):
+        x = make_inputs(w.replace(seed=seed))
+        return tuple(x[n].cuda() for n in "qkv")
+
+    q, k, v = load(w.seed + 1)
+    out = torch.empty_like(q)
+    fits = {}
+    for order in ("ascending", "diag_first"):
+        pts = []
+        for thr in grid:
+            ss.ss_attn_prefill_ex(q, k, v, out, scale=w.scale, causal=False, threshold=thr,
+                                  skip_mask=mask, order=order)
+            torch.cuda.synchronize()
+            s = skip_fraction(mask)
+            if 0.02 < s < 0.98:
+                pts.append((thr, L, s))
+        fits[order] = fit_factor(pts)
+    del q, k, v
+    q, k, v = load(w.seed)
+    fa = 4.0 * w.B * w.Hq * w.Lq * w.Lk * w.D
+    res = {"workload": "video_dit_32760 (B1 H24, 13x42x60 tokens, D128, non-causal)",
+           "calibration": "a*exp(b*s) fitted on replicate 1, timed on replicate 0"}
+    for order in ("ascending", "diag_first"):
+        a, b = fits[order]
+
+        def timed(th):
+            for _ in range(2):
+                ss.ss_attn_prefill_ex(q, k, v, out, scale=w.scale, causal=False, threshold=th,
+                                      skip_mask=mask, order=order)
+            steps = max(3, args.steps // 10)
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+            for e in evs:
+                evict_caches(args.flush)
+                e[0].record()
+                ss.ss_attn_prefill_ex(q, k, v, out, scale=w.scale, causal=False, threshold=th,
+                                      skip_mask=mask, order=order)
+                e[1].record()
+            torch.cuda.synchronize()
+            return sum(e[0].elapsed_time(e[1]) for e in evs) / steps, mask.cpu().numpy()
+
+        dense_ms, dmask = timed(0.0)
+        dense_out = out.clone()
+        thr, reachable = calibrated_threshold(a, b, 0.7, L)
+        ms, smask = timed(thr)
+        err = rel_l2(torch, out, dense_out)
+        fl_d, vis, _ = prefill_flops(dmask, w.D, w.Dv)
+        fl_s, _, kept = prefill_flops(smask, w.D, w.Dv)
+        gating = []
+        for t in (1.0, 0.6):
+            thr_t, _ = calibrated_threshold(a, b, 0.7, L, timestep=t, disabled_until=0.7)
+            ms_t, m_t = timed(thr_t)
+            gating.append({"timestep": t, "disabled_until": 0.7,
+                           "mode": "dense" if thr_t == 0 else "sparse",
+                           "threshold": float(f"{thr_t:.6g}"), "ms": round(ms_t, 3),
+                           "skip_fraction": round(float((m_t == 1).sum() / vis), 4)})
+        res[order] = {"a": float(f"{a:.6g}"), "b": float(f"{b:.6g}"), "target": 0.7,
+                      "threshold": float(f"{thr:.6g}"), "threshold_reaches_target": reachable,
+                      "skip_fraction": round(float((smask == 1).sum() / vis), 4),
+                      "ms": round(ms, 3), "dense_ms": round(dense_ms, 3),
+                      "speedup_vs_dense": round(dense_ms / ms, 3),
+                      "tflops_executed": round(fl_s / ms / 1e9, 1),
+                      "frac_of_bf16_peak": round(fl_s / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                      "dense_tflops_executed": round(fl_d / dense_ms / 1e9, 1),
+                      "dense_frac_of_bf16_peak": round(fl_d / dense_ms / 1e9 / BF16_PEAK_TFLOPS,
+                                                       4),
+                      "fa_convention_tflops": round(fa / ms / 1e9, 1),
+                      "rel_l2_vs_dense": float(f"{err:.3e}"), "gating": gating}
+        log(f"[video {order}] {res[order]}")
     return res
 
 
@@ -343,14 +466,33 @@ def bench_latent(ss, torch, args):
         return sum(e[0].elapsed_time(e[1]) for e in evs) / steps
 
     dense_ms = timed(0.0)
+    dense_out = out.clone()
     ms = timed(thr)
+    err = rel_l2(torch, out, dense_out)
     s = skip_at(thr)
+    import numpy as np
+
+    m = mask.cpu().numpy()
+    nK = m.shape[-1]
+    keys = np.full(nK, 128, dtype=np.int64)
+    keys[-1] = w.Lk - 128 * (nK - 1)
+    kept_keys = int(((m == 0) * keys[None, None, :]).sum())
     kbytes = w.B * w.Lk * 576 * 2
+    # MFMA work: Q.K^T over every key (576 wide), P.V over kept keys (512 wide)
+    flops = 2.0 * w.Hq * (w.B * w.Lk * 576 + kept_keys * 512)
+    dense_flops = 2.0 * w.Hq * w.B * w.Lk * (576 + 512)
     res = {"workload": f"{w.name} (B8 Hq128, one 576-wide latent head, value = first 512 "
-                       "columns)", "threshold": thr, "threshold_reaches_target": reachable,
+                       "columns)", "split_mode": "chained",
+           "threshold": thr, "threshold_reaches_target": reachable,
            "skip_fraction": round(s, 4), "ms": round(ms, 4), "dense_ms": round(dense_ms, 4),
            "k_gbs": round(kbytes / ms / 1e6, 1), "dense_k_gbs": round(kbytes / dense_ms / 1e6, 1),
-           "speedup_vs_dense": round(dense_ms / ms, 3)}
+           "frac_of_hbm_peak": round(kbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+           "dense_frac_of_hbm_peak": round(kbytes / dense_ms / 1e6 / HBM_PEAK_GBS, 4),
+           "mfma_tflops": round(flops / ms / 1e9, 1),
+           "frac_of_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+           "dense_frac_of_bf16_peak": round(dense_flops / dense_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+           "speedup_vs_dense": round(dense_ms / ms, 3),
+           "rel_l2_vs_dense": float(f"{err:.3e}")}
     log(f"[latent] {res}")
     return res
 
@@ -362,12 +504,26 @@ def cpu_baseline(dec, seconds):
     repeated until about ``seconds`` of CPU time."""
     import oracle
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} "
+                             f"({os.path.basename(i.get('filepath', ''))})" for i in info)
     except Exception:  # pragma: no cover - threadpoolctl is optional
         cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     w, x = dec["workload"], dec["x"]
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -380,7 +536,10 @@ def cpu_baseline(dec, seconds):
     by = decode_bytes(res["mask"], w.B, w.Hq, w.Hkv, w.Lk, w.D, w.Dv, dec["S"])
     tot = by["k"] + by["v_kept"] + by["q"] + by["out"]
     return {"value": round(tot * reps / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu_count": os.cpu_count(), "cpu_model": model,
+            "blas": blas,
+            "threads_note": "cores = BLAS threads; the oracle's per-tile loop is Python, so "
+                            "only its matrix products use more than one thread",
             "sample": f"the whole decode call ({w.B * w.Hkv} (batch, kv head) pairs, same "
                       f"threshold, one streaming pass as the chained splits decide) run "
                       f"{reps}x in {dt:.1f} s of fp64 numpy"}
@@ -430,7 +589,11 @@ def main():
                     help="use this decode threshold instead of calibrating")
     ap.add_argument("--prefill-threshold", type=float, default=None,
                     help="use this prefill threshold instead of calibrating")
+    ap.add_argument("--wide-threshold", type=float, default=None,
+                    help="use this threshold for the wide-gap (r=9) decode leg")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-wide-decode", action="store_true")
+    ap.add_argument("--no-video", action="store_true")
     ap.add_argument("--no-latent", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only-sparse-decode", action="store_true",
@@ -463,6 +626,7 @@ def main():
         return
     if args.only_sparse_decode:
         args.no_prefill = args.no_cpu = args.no_latent = args.no_backward = True
+        args.no_wide_decode = args.no_video = True
     args.flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     if args.only_latent:
         print(json.dumps({"latent": bench_latent(ss, torch, args)}), flush=True)
@@ -475,13 +639,17 @@ def main():
     w, by = dec["workload"], dec["bytes"]
     wall, kern, comb, warm = dec["sparse"]
     step_bytes = by["k"] + by["v_kept"] + by["q"] + by["out"]
-    kern_bytes = by["k"] + by["v_kept"] + by["q"] + by["partials"]
+    # the decode kernel's algorithmic bytes: K, the V of kept tiles and q (the
+    # call's out is written by the merge); the split partials it writes are
+    # implementation traffic, reported beside it, not counted
+    kern_bytes = by["k"] + by["v_kept"] + by["q"]
     achieved = kern_bytes / (kern * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_entry(kern_bytes),
             "kernel": "decode_gqa_kernel<128,4>", "kernel_ms": round(kern, 4),
-            "algorithmic_bytes_per_launch": kern_bytes}
+            "algorithmic_bytes_per_launch": kern_bytes,
+            "split_partial_bytes_per_launch": by["partials"]}
     line = {
         "metric": METRIC,
         "value": round(step_bytes / (wall * 1e-3) / 1e9, 1),
@@ -499,6 +667,7 @@ def main():
                    "skip_fraction": round(dec["skip"], 4), "num_splits": dec["S"],
                    "split_mode": "chained"},
         "roofline": roof,
+        "lookback_timeouts": dec["lookback_timeouts"],
     }
     if "dense" in dec:
         dwall, dkern, _, dwarm = dec["dense"]
@@ -506,10 +675,31 @@ def main():
         line["dense_ms_per_step"] = round(dwall, 4)
         dense_bytes = by["k"] + by["v_dense"] + by["q"] + by["out"]
         line["dense_value"] = round(dense_bytes / (dwall * 1e-3) / 1e9, 1)
+        line["rel_l2_vs_dense"] = float(f"{dec['rel_l2_vs_dense']:.3e}")
+    if not args.no_wide_decode:
+        wd = bench_decode(ss, torch, args, r=9.0)
+        wb = wd["bytes"]
+        wwall, wkern = wd["sparse"][0], wd["sparse"][1]
+        wstep = wb["k"] + wb["v_kept"] + wb["q"] + wb["out"]
+        wkb = wb["k"] + wb["v_kept"] + wb["q"]
+        line["decode_wide_gap"] = {
+            "generator": f"clustered keys r=9, {wd['workload'].n_c} centroids",
+            "threshold": wd["thr"], "threshold_reaches_target": wd["reachable"],
+            "skip_fraction": round(wd["skip"], 4), "ms_per_step": round(wwall, 4),
+            "gbs": round(wstep / (wwall * 1e-3) / 1e9, 1),
+            "kernel_gbs": round(wkb / (wkern * 1e-3) / 1e9, 1),
+            "kernel_frac_of_hbm_peak": round(wkb / (wkern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "dense_ms_per_step": round(wd["dense"][0], 4),
+            "speedup_vs_dense": round(wd["dense"][0] / wwall, 3),
+            "rel_l2_vs_dense": float(f"{wd['rel_l2_vs_dense']:.3e}"),
+            "lookback_timeouts": wd["lookback_timeouts"]}
+        del wd
     if not args.no_prefill:
         line["prefill"] = {"workload": "gqa_prefill_16k (B1 Hq32 Hkv8 L16384 D128 causal)",
                            "literal": bench_prefill(ss, torch, args, 3.0, "diag_first"),
                            "wide_gap": bench_prefill(ss, torch, args, 9.0, "diag_first")}
+    if not args.no_video:
+        line["video"] = bench_video(ss, torch, args)
     if not args.no_latent:
         line["latent"] = bench_latent(ss, torch, args)
     if not args.no_backward:
