@@ -63,8 +63,17 @@ __device__ __forceinline__ int k_slot(int r, int c) {
   return D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
 }
 
-template <int D, int NH>
+// QP = false: the NH = 2 row sets are two query heads of one KV group on one
+// query tile.  QP = true (group sizes that are odd, e.g. one query head per KV
+// head): the two row sets are two neighbouring query tiles of one head, and the
+// workgroup streams the key tiles both visit -- each set takes exactly its own
+// visit order out of the shared stream and sits out the steps it has no tile
+// in (a causal tile's sequence is one tile shorter than its upper
+// neighbour's; in diag_first order without causality the two rotations are
+// one tile apart, so the stream is one tile longer than either).
+template <int D, int NH, bool QP>
 __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(PrefillArgs a) {
+  static_assert(!QP || NH == 2, "query-tile pairs need two row sets");
   constexpr int NW = kRowWaves * NH;         // waves in the workgroup
   constexpr int KCH = D / 8;                 // 16-byte chunks per row
   constexpr int KS = D / 16;                 // MFMA k-steps over the head dimension
@@ -85,25 +94,38 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   __shared__ float red[NH][kRowWaves];
 
   const int nQ = (a.Lq + kTile - 1) / kTile;
-  // Logical order: (batch, KV head, query tile, head set within the group), so
-  // the head sets of one group on one query tile -- identical key/value tile
-  // sequences -- and then neighbouring query tiles are adjacent and, through
-  // xcd_local_order, share an XCD's L2.  Heaviest query tiles first when causal.
-  const int grp_sz = a.Hq / a.Hkv;
-  const int sets = grp_sz / NH;
-  const int L = xcd_local_order(blockIdx.x, gridDim.x);
-  const int hs = L % sets;
-  const int qi = (L / sets) % nQ;
-  const int hk = (L / (sets * nQ)) % a.Hkv;
-  const int b = L / (sets * nQ * a.Hkv);
-  const int qtile = a.causal ? nQ - 1 - qi : qi;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = w / kRowWaves;              // this wave's head within the set
+  const int hh = w / kRowWaves;              // this wave's row set
   const int wr = w % kRowWaves;              // this wave's 32-row block
-  const int head = hk * grp_sz + hs * NH + hh;
+  // Logical order: (batch, KV head, query tile, head set within the group) --
+  // QP: (batch, KV head, head within the group, query-tile pair) -- so work
+  // items that read the same key/value tiles at the same time are adjacent
+  // and, through xcd_local_order, share an XCD's L2.  Heaviest query tiles
+  // first when causal.
+  const int grp_sz = a.Hq / a.Hkv;
+  const int L = xcd_local_order(blockIdx.x, gridDim.x);
+  int hk, b, head, qtile, qpair = 0;
+  if constexpr (QP) {
+    const int nQP = (nQ + 1) / 2;
+    const int pi = L % nQP;
+    const int hin = (L / nQP) % grp_sz;
+    hk = (L / (nQP * grp_sz)) % a.Hkv;
+    b = L / (nQP * grp_sz * a.Hkv);
+    qpair = a.causal ? nQP - 1 - pi : pi;
+    head = hk * grp_sz + hin;
+    qtile = 2 * qpair + hh;
+  } else {
+    const int sets = grp_sz / NH;
+    const int hs = L % sets;
+    const int qi = (L / sets) % nQ;
+    hk = (L / (sets * nQ)) % a.Hkv;
+    b = L / (sets * nQ * a.Hkv);
+    qtile = a.causal ? nQ - 1 - qi : qi;
+    head = hk * grp_sz + hs * NH + hh;
+  }
+  const bool qtile_ok = qtile < nQ;  // QP with an odd tile count: the last pair's upper set is empty
   const int l32 = lane & 31;
   const int g = lane >> 5;  // MFMA k-group of this lane
   const int row0 = qtile * kTile;
@@ -116,10 +138,48 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   const unsigned short* vp =
       static_cast<const unsigned short*>(a.v) + ((size_t)(b * a.Hkv + hk) * a.Lk) * D;
 
-  const VisitPlan plan = make_visit_plan(qtile, a.Lq, a.Lk, a.causal, a.order);
+  const VisitPlan plan = make_visit_plan(qtile_ok ? qtile : nQ - 1, a.Lq, a.Lk, a.causal, a.order);
   const int nK = plan.nK;
+  const int count = qtile_ok ? plan.count : 0;  // tiles this row set visits
+  // The stream of key tiles the workgroup loads: U steps; this row set takes
+  // its visit t at stream step u0 + t.
+  int U = count, u0 = 0;
+  VisitPlan pl0 = plan, pl1 = plan;
+  int c0 = count, c1 = count, s0 = 0, s1 = 0;
+  if constexpr (QP) {
+    const int q0 = 2 * qpair, q1 = 2 * qpair + 1;
+    pl0 = make_visit_plan(q0, a.Lq, a.Lk, a.causal, a.order);
+    pl1 = make_visit_plan(q1 < nQ ? q1 : q0, a.Lq, a.Lk, a.causal, a.order);
+    c0 = pl0.count;
+    c1 = q1 < nQ ? pl1.count : 0;
+    if (a.causal) {
+      // both end on tile 0 (diag_first) or start on it (ascending)
+      U = max(c0, c1);
+      if (a.order == SS_ORDER_DIAG_FIRST) {
+        s0 = U - c0;
+        s1 = U - c1;
+      }
+    } else if (a.order == SS_ORDER_DIAG_FIRST && c1 > 0 && pl1.start != pl0.start) {
+      // rotations one tile apart: start_1 = start_0 + 1
+      U = c0 + 1;
+      s1 = 1;
+    } else {
+      U = max(c0, c1);
+    }
+    u0 = hh == 0 ? s0 : s1;
+  }
+  // the key tile of stream step u
+  auto stream_tile = [&](int u) __attribute__((always_inline)) {
+    if constexpr (QP) {
+      const int t0 = u - s0;
+      return (t0 >= 0 && t0 < c0) ? pl0.tile_at(t0) : pl1.tile_at(u - s1);
+    } else {
+      return plan.tile_at(u);
+    }
+  };
   // this head's mask row; its first wave writes it
-  uint8_t* const mrow = a.mask ? a.mask + ((size_t)(b * a.Hq + head) * nQ + qtile) * nK : nullptr;
+  uint8_t* const mrow =
+      a.mask && qtile_ok ? a.mask + ((size_t)(b * a.Hq + head) * nQ + qtile) * nK : nullptr;
   const bool mask_writer = mrow && wr == 0;
   if (mask_writer && plan.causal)
     for (int j = plan.last + 1 + lane; j < nK; j += 64) mrow[j] = 2;
@@ -218,23 +278,29 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   // image uses dual_slot, which keeps 32 lanes of a transpose read on
   // different banks (the swizzle it replaced did so for 16 lanes only).
 
-  if (plan.count > 0) issue_tile(plan.tile_at(0), 0);
+  if (U > 0) issue_tile(stream_tile(0), 0);
 
-  // one tile, from ring stage t & 1
-  for (int t = 0; t < plan.count; ++t) {
-    const int st = t & 1;
+  // one stream step, from ring stage u & 1; the row set works on it when it
+  // holds one of its own visits (always, unless QP)
+  for (int u = 0; u < U; ++u) {
+    const int st = u & 1;
     const unsigned char* Ks = kst[st];
     const unsigned char* Vs = vst[st];
-    const int j = plan.tile_at(t);
+    const int t = u - u0;  // this row set's visit
+    const bool active = !QP || (t >= 0 && t < count);
+    const int j = active ? plan.tile_at(t) : 0;
     const int j0 = j * kTile;
     // this tile's loads have landed (own wave), and every wave is past tile t-1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // the stage of tile t-1 is free: start tile t+1
-    if (t + 1 < plan.count) issue_tile(plan.tile_at(t + 1), st ^ 1);
+    if (u + 1 < U) issue_tile(stream_tile(u + 1), st ^ 1);
 
-    // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 rows
     f32x16_t sacc[4];
+    float tmax2 = neg_inf();
+    bool row_skip = false;
+    if (active) {
+    // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 rows
     const int koff0 = koff_now();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -275,15 +341,17 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
     tmax = max_xor32(tmax);
-    const float tmax2 = tmax * c;
+    tmax2 = tmax * c;
 
     float delta = neg_inf();
     if (row_ok && tmax2 != neg_inf()) delta = (m2 == neg_inf()) ? pos_inf() : tmax2 - m2;
-    const bool row_skip = delta < a.log2_thr;  // this row's own test
+    row_skip = delta < a.log2_thr;  // this row's own test
     if (row_writer) rrow()[j] = row_skip ? 1 : 0;
     delta = wave_max(delta);
     if (lane == 0) red[hh][wr] = delta;
+    }
     __syncthreads();  // red[] visible
+    if (active) {
     float dblk = red[hh][0];
 #pragma unroll
     for (int i = 1; i < kRowWaves; ++i) dblk = fmaxf(dblk, red[hh][i]);
@@ -351,6 +419,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
       }
     }
     m2 = m2n;
+    }
   }
 
   // ---- epilogue: O / l, lane holds columns 32 mb + 8 (i/4) + 4 g + i%4 of row rq
@@ -378,18 +447,22 @@ bool prefill_bf16_supported(int D, int Dv) { return D == Dv && (D == 64 || D == 
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const int nQ = (a.Lq + kTile - 1) / kTile;
-  const int nh = ((a.Hq / a.Hkv) % 2 == 0) ? 2 : 1;  // heads per workgroup
-  const dim3 grid((unsigned)((size_t)nQ * (a.Hq / nh) * a.B));
+  // two heads of a KV group per workgroup when the group size is even, else
+  // two neighbouring query tiles of one head
+  const bool pairs_of_heads = (a.Hq / a.Hkv) % 2 == 0;
+  const dim3 block(64 * kRowWaves * 2);
+  const dim3 grid(pairs_of_heads ? (unsigned)((size_t)nQ * (a.Hq / 2) * a.B)
+                                 : (unsigned)((size_t)((nQ + 1) / 2) * a.Hq * a.B));
   if (a.D == 64) {
-    if (nh == 2)
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, 2>), grid, dim3(64 * kRowWaves * 2), 0, s, a);
+    if (pairs_of_heads)
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, 2, false>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, 1>), grid, dim3(64 * kRowWaves), 0, s, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, 2, true>), grid, block, 0, s, a);
   } else {
-    if (nh == 2)
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, 2>), grid, dim3(64 * kRowWaves * 2), 0, s, a);
+    if (pairs_of_heads)
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, false>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, 1>), grid, dim3(64 * kRowWaves), 0, s, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, true>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -98,6 +98,14 @@ PREFILL_CASES = [
     ("dense", 1, 4, 1, 1000, 1000, 128, True, "ascending", 3.0, 0.0),
     ("single_tile", 1, 1, 1, 100, 100, 64, True, "ascending", 3.0, 0.5),
     ("one_query_row", 1, 1, 1, 1, 300, 128, True, "ascending", 9.0, 0.1),
+    # odd group sizes run two neighbouring query tiles of one head per
+    # workgroup over a shared key stream: odd tile counts, Lq != Lk, both
+    # orders, causal and not
+    ("mha_causal_diag_lq_below_lk", 1, 2, 2, 650, 1100, 128, True, "diag_first", 9.0, 0.1),
+    ("mha_noncausal_diag_lq_below_lk", 1, 3, 3, 700, 1300, 64, False, "diag_first", 9.0, 0.05),
+    ("mha_noncausal_diag_lq_above_lk", 1, 1, 1, 1300, 700, 128, False, "diag_first", 9.0, 0.05),
+    ("mha_causal_asc_odd_tiles", 1, 1, 1, 1100, 1100, 128, True, "ascending", 9.0, 0.1),
+    ("gqa3_causal_diag_odd_tiles", 1, 6, 2, 1100, 1100, 128, True, "diag_first", 9.0, 0.05),
 ]
 
 
