@@ -512,7 +512,7 @@ int ss_attn_decode_paged(const ss_decode_paged_params* p, hipStream_t stream) {
   const int group = p->Hq / p->Hkv;
   if (decode_kernel(p->D, p->Dv, group, false) != DecodeKernel::kGqa)
     return fail(SS_ERR_UNSUPPORTED, "paged decode supports D == Dv in {64, 128} and Hq/Hkv in "
-                "{1, 2, 4, 8} (got D=%d Dv=%d group=%d)", p->D, p->Dv, group);
+                "1..8, 16 or 32 (got D=%d Dv=%d group=%d)", p->D, p->Dv, group);
   const DecodePlan pl =
       plan_decode(p->B, p->Hq, p->Hkv, p->max_seq_len, p->D, p->Dv, false, p->num_splits, true);
   if (!p->workspace || p->workspace_bytes < pl.bytes)

@@ -48,27 +48,44 @@ constexpr int kKeysPerWave = kTile / kWaves;  // 32
 constexpr int kSpinCap = 1 << 21;             // look-back polls before giving up
 constexpr int kWavesPerSimd = 3;              // occupancy target: 3 workgroups per CU
 
+// Score area: 128 keys x G rows x 4 bytes per tile, 32 KB (64 KB past eight
+// rows, where one workgroup holds the compute unit anyway).
 template <int G>
-constexpr int max_tiles() { return 64 / G; }  // score LDS: 128 keys x G x 4 B x tiles = 32 KB
+constexpr int max_tiles() { return (G <= 8 ? 64 : 128) / G; }
+// Query-head columns of one 16x16x32 MFMA block, and the rows one V-pass
+// round accumulates (a lane holds 8 value columns of each).
+template <int G>
+constexpr int col_blocks() { return (G + 15) / 16; }
+template <int G>
+constexpr int v_rows() { return G < 16 ? G : 16; }
+// Workgroups per compute unit the registers allow.
+template <int D, int G>
+constexpr int wg_per_cu() { return G <= 4 ? kWavesPerSimd : G <= 8 ? (D == 128 ? 2 : kWavesPerSimd) : 1; }
 
 typedef __attribute__((ext_vector_type(4))) float f4_t;
 
 template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) void decode_gqa_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, (wg_per_cu<D, G>())) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int TMAX = max_tiles<G>();
+  constexpr int CB = col_blocks<G>();  // K pass: MFMA column blocks
+  constexpr int GR = v_rows<G>();      // V pass: rows per round
+  constexpr int RH = G / GR;           // V pass: rounds
+  constexpr unsigned kAllRows = G == 32 ? ~0u : (1u << G) - 1u;
   constexpr int KS = D / 32;          // MFMA k-steps over the head dimension
   constexpr int KL = 2 * KS;          // 16-byte K loads per lane per tile
   constexpr int KCH = D / 8;          // V pass: lanes per value row
   constexpr int KPI = 64 / KCH;       // V pass: keys per wave instruction
   constexpr int IT = kKeysPerWave / KPI;
-  static_assert(G >= 1 && G <= 8 && TMAX <= 64, "group");
-  static_assert(kWaves * G * D <= TMAX * kTile * G, "reduction reuses the score area");
+  static_assert(G >= 1 && G <= 32 && TMAX <= 64 && RH * GR == G, "group");
+  static_assert(RH > 1 || kWaves * GR * D <= TMAX * kTile * G, "reduction reuses the score area");
 
   __shared__ __attribute__((aligned(16))) float sc[TMAX * kTile * G];  // [tile][key][row]
   __shared__ __attribute__((aligned(16))) unsigned char kstage[kWaves][16 * D * 2];
   __shared__ float tpart[kWaves][TMAX][G];
   __shared__ float s_mref[G];
-  __shared__ float s_lred[kWaves][G];
+  __shared__ float s_lred[kWaves][GR];
+  // several V rounds read the scores again: their reduction area is separate
+  __shared__ __attribute__((aligned(16))) float red_sep[RH > 1 ? kWaves * GR * D : 1];
   __shared__ int s_surv[TMAX];
   __shared__ unsigned s_rowkeep[TMAX];  // per kept tile: bit r = row r adds its P
   __shared__ int s_nsurv;
@@ -149,14 +166,18 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
 
   // ---------------------------------------------------------------- 1. K pass
   {
-    // Q^T as the MFMA B operand: lane holds row l16 (zero past G), dims 32 ks + 8 grp
-    bf16x8_t qb[KS];
+    // Q^T as the MFMA B operand: in column block cb lane holds row
+    // 16 cb + l16 (zero past G), dims 32 ks + 8 grp
+    bf16x8_t qb[CB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t u = {0u, 0u, 0u, 0u};
-      if (l16 < G) u = *reinterpret_cast<const u32x4_t*>(qp + (size_t)l16 * D + ks * 32 + grp * 8);
-      qb[ks] = as_bf16x8(u);
-    }
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r = cb * 16 + l16;
+        u32x4_t u = {0u, 0u, 0u, 0u};
+        if (r < G) u = *reinterpret_cast<const u32x4_t*>(qp + (size_t)r * D + ks * 32 + grp * 8);
+        qb[cb][ks] = as_bf16x8(u);
+      }
     // coalesced K loads: load i covers rows [i*RPI, (i+1)*RPI) of the wave's 32
     constexpr int RPI = 64 / KCH;  // key rows per wave instruction
     const int lrow = lane / KCH, lch = lane % KCH;
@@ -175,7 +196,7 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
     auto score_tile = [&](int tl, const u32x4_t (&src)[KL]) {
       // the wave's 32 rows go through the stage 16 at a time (one MFMA block);
       // 16-byte chunk c of stage row r sits at chunk c ^ (r & 7)
-      f32x4_t acc[2];
+      f32x4_t acc[CB][2];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
@@ -184,32 +205,39 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
           *reinterpret_cast<u32x4_t*>(stage + r * (D * 2) + ((lch ^ (r & 7)) << 4)) = src[i];
         }
         __builtin_amdgcn_wave_barrier();
-        acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[cb][blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int ch = ks * 4 + grp;
           const u32x4_t kv =
               *reinterpret_cast<const u32x4_t*>(stage + l16 * (D * 2) + ((ch ^ (l16 & 7)) << 4));
-          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qb[ks], acc[blk], 0,
-                                                            0, 0);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[cb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qb[cb][ks],
+                                                                  acc[cb][blk], 0, 0, 0);
         }
         __builtin_amdgcn_wave_barrier();
       }
       const int jw = (t0 + tl) * kTile + w * kKeysPerWave;  // first key of this wave
-      float pm = neg_inf();
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+      for (int cb = 0; cb < CB; ++cb) {
+        const int r = cb * 16 + l16;  // this lane's query row
+        float pm = neg_inf();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kin = blk * 16 + grp * 4 + i;  // key within the wave's 32
-          float s = acc[blk][i] * c;
-          if (jw + kin >= Lk) s = neg_inf();
-          if (l16 < G) sc[(tl * kTile + w * kKeysPerWave + kin) * G + l16] = s;
-          pm = fmaxf(pm, s);
-        }
-      pm = fmaxf(pm, shfl_xor_f(pm, 16));
-      pm = fmaxf(pm, shfl_xor_f(pm, 32));
-      if (lane < G) tpart[w][tl][lane] = pm;
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kin = blk * 16 + grp * 4 + i;  // key within the wave's 32
+            float s = acc[cb][blk][i] * c;
+            if (jw + kin >= Lk) s = neg_inf();
+            if (r < G) sc[(tl * kTile + w * kKeysPerWave + kin) * G + r] = s;
+            pm = fmaxf(pm, s);
+          }
+        pm = fmaxf(pm, shfl_xor_f(pm, 16));
+        pm = fmaxf(pm, shfl_xor_f(pm, 32));
+        if (lane < 16 && r < G) tpart[w][tl][r] = pm;
+      }
     };
     // three tiles of K in flight per wave; prefetches past the last tile
     // re-read the last tile (cache hits) and are not used
@@ -307,7 +335,7 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
     const int idx = __popcll(bits & ((1ull << lane) - 1ull));
     if (kept) s_surv[idx] = lane;
     if constexpr (!PAGED) {
-      if (valid) s_rowkeep[lane] = a.per_row ? rowkeep : 0xffu;
+      if (valid) s_rowkeep[lane] = a.per_row ? rowkeep : kAllRows;
       if (valid && a.row_mask) {
 #pragma unroll
         for (int r = 0; r < G; ++r)
@@ -324,116 +352,143 @@ __global__ __launch_bounds__(kThreads, G == 8 && D == 128 ? 2 : kWavesPerSimd) v
   __syncthreads();
 
   // ---------------------------------------------------------------- 3. V pass
+  // rows [rb, rb + GR) per round; more than one round (past 16 rows) reads
+  // the kept V rows again, from L2
   const int kq = lane / KCH;
   const int cc = lane % KCH;
   const int nsurv = s_nsurv;
-  float mref[G], o[G][8], lp[G];
 #pragma unroll
-  for (int r = 0; r < G; ++r) {
-    mref[r] = s_mref[r];
-    lp[r] = 0.f;
+  for (int rh = 0; rh < RH; ++rh) {
+    const int rb = rh * GR;
+    float mref[GR], o[GR][8], lp[GR];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
-  }
-  {
-    // unconditional loads as in the K pass; keys past Lk carry p = 0
-    auto load_v = [&](int si, u32x4_t (&dst)[IT]) {
-      const int j0 = (t0 + s_surv[si]) * kTile + w * kKeysPerWave;
+    for (int r = 0; r < GR; ++r) {
+      mref[r] = s_mref[rb + r];
+      lp[r] = 0.f;
 #pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int key = min(j0 + it * KPI + kq, Lk - 1);
-        dst[it] = *reinterpret_cast<const u32x4_t*>(row(vp, key) + cc * 8);
-      }
-    };
-    auto accum_v = [&](int si, const u32x4_t (&src)[IT]) {
-      const int tl = s_surv[si];
-      // rows that did not pass on this tile (per-row decisions) take +inf as
-      // their exponent reference: P = 0
-      const unsigned keep = PAGED ? 0xffu : s_rowkeep[tl];
-      float mx[G];
+      for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+    }
+    {
+      // unconditional loads as in the K pass; keys past Lk carry p = 0
+      auto load_v = [&](int si, u32x4_t (&dst)[IT]) {
+        const int j0 = (t0 + s_surv[si]) * kTile + w * kKeysPerWave;
 #pragma unroll
-      for (int r = 0; r < G; ++r) mx[r] = (keep >> r) & 1u ? mref[r] : pos_inf();
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int kin = w * kKeysPerWave + it * KPI + kq;
-        const float* srow = sc + (tl * kTile + kin) * G;
-        float p[G];
-        if constexpr (G == 4) {
-          const f4_t s4 = *reinterpret_cast<const f4_t*>(srow);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s4[r] - mx[r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < G; ++r) p[r] = fast_exp2(srow[r] - mx[r]);
+        for (int it = 0; it < IT; ++it) {
+          const int key = min(j0 + it * KPI + kq, Lk - 1);
+          dst[it] = *reinterpret_cast<const u32x4_t*>(row(vp, key) + cc * 8);
         }
-        float vf[8];
+      };
+      auto accum_v = [&](int si, const u32x4_t (&src)[IT]) {
+        const int tl = s_surv[si];
+        // rows that did not pass on this tile (per-row decisions) take +inf
+        // as their exponent reference: P = 0
+        const unsigned keep = PAGED ? kAllRows : s_rowkeep[tl];
+        float mx[GR];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[2 * e] = bf16_lo(src[it][e]);
-          vf[2 * e + 1] = bf16_hi(src[it][e]);
+        for (int r = 0; r < GR; ++r) mx[r] = (keep >> (rb + r)) & 1u ? mref[r] : pos_inf();
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int kin = w * kKeysPerWave + it * KPI + kq;
+          const float* srow = sc + (tl * kTile + kin) * G + rb;
+          float p[GR];
+          if constexpr (G == 4) {
+            const f4_t s4 = *reinterpret_cast<const f4_t*>(srow);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s4[r] - mx[r]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < GR; ++r) p[r] = fast_exp2(srow[r] - mx[r]);
+          }
+          float vf[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vf[2 * e] = bf16_lo(src[it][e]);
+            vf[2 * e + 1] = bf16_hi(src[it][e]);
+          }
+#pragma unroll
+          for (int r = 0; r < GR; ++r) {
+            lp[r] += p[r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[r][e] = fmaf(p[r], vf[e], o[r][e]);
+          }
         }
-#pragma unroll
-        for (int r = 0; r < G; ++r) {
-          lp[r] += p[r];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[r][e] = fmaf(p[r], vf[e], o[r][e]);
+      };
+      if constexpr (G <= 8) {
+        if (nsurv > 0) {  // three survivor tiles of V in flight per wave
+          u32x4_t vA[IT], vB[IT], vC[IT];
+          load_v(0, vA);
+          load_v(min(1, nsurv - 1), vB);
+          for (int si = 0; si < nsurv; si += 3) {
+            load_v(min(si + 2, nsurv - 1), vC);
+            accum_v(si, vA);
+            load_v(min(si + 3, nsurv - 1), vA);
+            if (si + 1 < nsurv) accum_v(si + 1, vB);
+            load_v(min(si + 4, nsurv - 1), vB);
+            if (si + 2 < nsurv) accum_v(si + 2, vC);
+          }
         }
-      }
-    };
-    if (nsurv > 0) {  // three survivor tiles of V in flight per wave
-      u32x4_t vA[IT], vB[IT], vC[IT];
-      load_v(0, vA);
-      load_v(min(1, nsurv - 1), vB);
-      for (int si = 0; si < nsurv; si += 3) {
-        load_v(min(si + 2, nsurv - 1), vC);
-        accum_v(si, vA);
-        load_v(min(si + 3, nsurv - 1), vA);
-        if (si + 1 < nsurv) accum_v(si + 1, vB);
-        load_v(min(si + 4, nsurv - 1), vB);
-        if (si + 2 < nsurv) accum_v(si + 2, vC);
+      } else {
+        if (nsurv > 0) {  // the accumulators of 16 rows leave room for two tiles in flight
+          u32x4_t vA[IT], vB[IT];
+          load_v(0, vA);
+          for (int si = 0; si < nsurv; si += 2) {
+            load_v(min(si + 1, nsurv - 1), vB);
+            accum_v(si, vA);
+            load_v(min(si + 2, nsurv - 1), vA);
+            if (si + 1 < nsurv) accum_v(si + 1, vB);
+          }
+        }
       }
     }
-  }
-  __syncthreads();  // the reduction below overwrites the score area
-
-  // ---------------------------------------------------------------- merge and write
-  float* red = sc;  // [wave][row][D]
+    // ------------------------------------------------------------ merge and write
+    float* red = RH > 1 ? red_sep : sc;  // [wave][row][D]
+    __syncthreads();  // a single round's reduction overwrites the score area; the previous round's is read
 #pragma unroll
-  for (int r = 0; r < G; ++r) {
-    const float lr = lanes_sum_from<KCH>(lp[r]);
+    for (int r = 0; r < GR; ++r) {
+      const float lr = lanes_sum_from<KCH>(lp[r]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[r][e] = lanes_sum_from<KCH>(o[r][e]);
-    if (kq == 0) {
+      for (int e = 0; e < 8; ++e) o[r][e] = lanes_sum_from<KCH>(o[r][e]);
+      if (kq == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[(w * G + r) * D + cc * 8 + e] = o[r][e];
+        for (int e = 0; e < 8; ++e) red[(w * GR + r) * D + cc * 8 + e] = o[r][e];
+      }
+      if (lane == 0) s_lred[w][r] = lr;
     }
-    if (lane == 0) s_lred[w][r] = lr;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int r = idx / D, dv = idx % D;
-    float ov = 0.f, l = 0.f;
+    __syncthreads();
+    for (int idx = tid; idx < GR * D; idx += kThreads) {
+      const int r = idx / D, dv = idx % D;
+      float ov = 0.f, l = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      ov += red[(ww * G + r) * D + dv];
-      l += s_lred[ww][r];
+      for (int ww = 0; ww < kWaves; ++ww) {
+        ov += red[(ww * GR + r) * D + dv];
+        l += s_lred[ww][r];
+      }
+      const size_t rowid = ((size_t)sub * a.B + b) * a.Hq + hk * G + rb + r;
+      a.part_o[rowid * D + dv] = l > 0.f ? ov / l : 0.f;
+      if (dv == 0) a.part_lse[rowid] = l > 0.f ? (s_mref[rb + r] + __log2f(l)) * kLn2 : neg_inf();
     }
-    const size_t rowid = ((size_t)sub * a.B + b) * a.Hq + hk * G + r;
-    a.part_o[rowid * D + dv] = l > 0.f ? ov / l : 0.f;
-    if (dv == 0) a.part_lse[rowid] = l > 0.f ? (s_mref[r] + __log2f(l)) * kLn2 : neg_inf();
   }
 }
 
 template <int D, bool PAGED>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s, int G) {
   const dim3 grid((unsigned)((size_t)a.num_splits * a.Hkv * a.B));
+#define SSATTN_DECODE_CASE(g) \
+  case g: hipLaunchKernelGGL((decode_gqa_kernel<D, g, PAGED>), grid, dim3(kThreads), 0, s, a); break;
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_gqa_kernel<D, 1, PAGED>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_gqa_kernel<D, 2, PAGED>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_gqa_kernel<D, 4, PAGED>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_gqa_kernel<D, 8, PAGED>), grid, dim3(kThreads), 0, s, a); break;
+    SSATTN_DECODE_CASE(1)
+    SSATTN_DECODE_CASE(2)
+    SSATTN_DECODE_CASE(3)
+    SSATTN_DECODE_CASE(4)
+    SSATTN_DECODE_CASE(5)
+    SSATTN_DECODE_CASE(6)
+    SSATTN_DECODE_CASE(7)
+    SSATTN_DECODE_CASE(8)
+    SSATTN_DECODE_CASE(16)
+    SSATTN_DECODE_CASE(32)
     default: return hipErrorInvalidValue;
   }
+#undef SSATTN_DECODE_CASE
   return hipGetLastError();
 }
 
@@ -441,10 +496,10 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s, int G) {
 
 bool decode_gqa_supported(int D, int Dv, int group, bool latent) {
   return !latent && D == Dv && (D == 64 || D == 128) &&
-         (group == 1 || group == 2 || group == 4 || group == 8);
+         ((group >= 1 && group <= 8) || group == 16 || group == 32);
 }
 
-int decode_gqa_max_tiles(int group) { return 64 / group; }
+int decode_gqa_max_tiles(int group) { return (group <= 8 ? 64 : 128) / group; }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;

@@ -229,8 +229,10 @@ typedef enum { SS_SPLIT_CHAINED = 0, SS_SPLIT_INDEPENDENT = 1 } ss_split_mode;
  * `workspace` is caller-owned device memory of at least
  * ss_attn_decode_workspace_bytes() bytes; its contents on entry do not
  * matter, and two calls that overlap in time must not share one.  Supported:
- * (D, Dv) = (64, 64) or (128, 128) with Hq/Hkv in {1, 2, 4, 8}; (576, 512)
- * with v == NULL and Hq/Hkv in {64, 128}.
+ * (D, Dv) = (64, 64) or (128, 128) with Hq/Hkv in 1..8, 16 or 32 (multi-head,
+ * grouped-query and multi-query attention: the BLASST summary, "Belangrijkste
+ * Bijdragen", names MHA, GQA, MQA and MLA); (576, 512) with v == NULL and
+ * Hq/Hkv in {64, 128} (a shared latent cache).
  *
  * ss_attn_decode is ss_attn_decode_ex with split_mode CHAINED.
  */

@@ -98,6 +98,8 @@ PAGED_CASES = [
     ("dense", [1000, 3000], 8, 2, 128, 16, 3.0, 0.0, None, 0),
     ("many_splits", [5000, 100, 2600], 8, 2, 128, 16, 9.0, 40.0, None, 40),
     ("long_chain_g1", [20000, 7000], 2, 2, 128, 128, 9.0, 200.0, None, 0),
+    ("gqa5_bs32", [3000, 129, 1700], 10, 2, 128, 32, 9.0, 60.0, None, 0),
+    ("mqa16_bs16", [4000, 1000], 16, 1, 128, 16, 9.0, 60.0, None, 0),
 ]
 
 

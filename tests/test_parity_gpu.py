@@ -236,6 +236,17 @@ DECODE_CASES = [
     ("one_key", 1, 2, 2, 1, 128, 1, 3.0, 0.1),
     ("gqa2_many_splits", 1, 4, 2, 2500, 128, 99, 9.0, 0.05),
     ("g1_long_chain", 1, 2, 2, 20000, 128, 0, 9.0, 0.02),
+    # other group sizes: 3..7 query heads per KV head, and multi-query
+    # attention with 16 or 32 heads on one KV head
+    ("gqa3_d64", 2, 6, 2, 3000, 64, 0, 9.0, 0.05),
+    ("gqa5_ragged", 1, 10, 2, 2777, 128, 3, 9.0, 0.1),
+    ("mqa6", 2, 6, 1, 5000, 128, 0, 9.0, 0.05),
+    ("gqa7", 1, 14, 2, 1500, 128, 2, 9.0, 0.2),
+    ("mqa16", 2, 16, 1, 6000, 128, 0, 9.0, 0.05),
+    ("mqa16_dense_one_split", 1, 16, 1, 1000, 128, 1, 3.0, 0.0),
+    ("mqa32", 2, 32, 1, 6000, 128, 0, 9.0, 0.05),
+    ("mqa32_d64_thr1", 1, 32, 1, 3000, 64, 4, 9.0, 1.0),
+    ("mqa32_long_chain", 1, 32, 1, 20000, 128, 0, 9.0, 0.02),
 ]
 
 

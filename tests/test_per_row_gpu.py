@@ -201,6 +201,8 @@ DECODE_ROW_CASES = [
     ("mha", 2, 4, 4, 1500, 128, 2, 9.0, 0.3),
     ("thr_above_one", 1, 8, 2, 2000, 128, 3, 3.0, 2.0),
     ("g1_long_chain", 1, 2, 2, 20000, 128, 0, 9.0, 0.02),
+    ("gqa6", 2, 12, 2, 3000, 128, 0, 9.0, 0.05),
+    ("mqa32", 1, 32, 1, 4000, 128, 0, 9.0, 0.05),
 ]
 
 
