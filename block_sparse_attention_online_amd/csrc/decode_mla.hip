@@ -32,12 +32,19 @@
 //
 //  * threshold 0: one online pass (running max, rescale when it has grown by
 //    more than 2^8 -- P stays below 256, exactly representable scaling).
-//  * threshold > 0: a score pass over the sub-split records every head's
-//    tile maxima (LDS table); the decision folds in the maxima of the earlier
-//    sub-splits of the chain (published per head, each read with a launch
-//    tag), so the decisions are those of one streaming pass over the chain;
-//    then the kept tiles are read again, scored, exponentiated against the
-//    sub-split's own per-head max (no rescaling) and multiplied by V.
+//  * threshold > 0, sub-splits that are whole chains (independent splits, or
+//    one split): a single streaming pass (stream mode below).  Each tile is
+//    scored and decided against the running max of the tiles before it in
+//    the chain; a kept tile is read once more a few steps later, while its
+//    bytes are still in the device's last-level cache, scored again and
+//    multiplied by V.  No tile is read from HBM twice.
+//  * threshold > 0, chains cut into several sub-splits: a score pass over
+//    the sub-split records every head's tile maxima (LDS table); the decision
+//    folds in the maxima of the earlier sub-splits of the chain (published
+//    per head, each read with a launch tag), so the decisions are those of
+//    one streaming pass over the chain; then the kept tiles are read again,
+//    scored, exponentiated against the sub-split's own per-head max (no
+//    rescaling) and multiplied by V.
 //
 // The split's O / l and lse go to the workspace; decode_combine merges splits.
 
@@ -61,6 +68,7 @@ constexpr int kUnits = kStepBytes / 1024;                // 1 KB wave load instr
 constexpr int kQk = kDqk / 16;                           // 36 MFMA k-steps over the key width
 constexpr int kVb = kDv / 32;                            // 16 value-column blocks
 constexpr float kRescaleMargin = 8.f;                    // log2 units (P < 256)
+constexpr float kStreamMargin = 64.f;                    // log2 units, stream mode
 constexpr int kSpinCap = 1 << 21;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -117,10 +125,17 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16_t& x, f32x16_t& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
 
-// SHARE: stage 2 of a thresholded decode (this workgroup's share of the
-// sequence's kept tiles, from the planning launch); otherwise stage 0 or 1.
-template <int NW, bool SHARE>
+// Kernel modes.  kModeSplit: stage 0 or 1 (a.mla_stage); kModeShare: stage 2
+// of a thresholded decode (this workgroup's share of the sequence's kept
+// tiles, from the planning launch); kModeStream: the single streaming pass of
+// a thresholded decode whose sub-splits are whole chains.
+constexpr int kModeSplit = 0;
+constexpr int kModeShare = 1;
+constexpr int kModeStream = 2;
+
+template <int NW, int MODE>
 __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
+  constexpr bool SHARE = MODE == kModeShare;
   constexpr int G = NW * kHeadsPerWave;  // heads per latent head
   constexpr int kThreads = 64 * NW;
   constexpr int LPW = kUnits / NW;       // load instructions per wave per step
@@ -289,12 +304,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
     return acc[0];
   };
 
-  // raw scores of keys past Lk -> -inf (only the tail step of a sequence)
+  // raw scores of keys past Lk -> -inf (only the tail step of a sequence;
+  // the lane's key offset is computed there, not kept live across the loop)
   auto mask_tail = [&](f32x16_t& s, int key0) __attribute__((always_inline)) {
     if (key0 + kStepKeys > a.Lk) {
+      const int k0 = key0 + 4 * (lane_id_fresh() >> 5);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (key0 + 8 * (i >> 2) + 4 * g + (i & 3) >= a.Lk) s[i] = neg_inf();
+        if (k0 + 8 * (i >> 2) + (i & 3) >= a.Lk) s[i] = neg_inf();
     }
   };
 
@@ -399,6 +416,174 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   float mref = neg_inf();  // exponent reference of head myhead (log2 units)
   int nkept = T;
 
+  if constexpr (MODE == kModeStream) {
+    // ---------------------------------------------------------- stream pass
+    // The sub-split is a whole chain.  Steps, in the order they run:
+    //   K(u, 0..3)  tile u's four score steps; K(u, 3) decides tile u from
+    //               every head's tile max against its running max and folds
+    //               the tile max into it
+    //   R(u, 0..3)  only for a kept tile u, right after K(u + 1, 2): the tile
+    //               is read again (from the last-level cache: it came from
+    //               HBM four to seven steps earlier), scored, exponentiated
+    //               and multiplied by V
+    //   after the last tile: three empty steps, then its R steps if kept.
+    // Loads run three steps ahead in a four-slot ring, so the step after
+    // K(u + 1, 2) is issued at the barrier of K(u + 1, 0): the first point
+    // at which every wave can read tile u's decision, written to LDS (one
+    // value per wave, the max over its heads) in K(u, 3).
+    constexpr int kRing = 4;
+    constexpr int kAhead = kRing - 1;
+    static_assert(kStepsPerTile == kRing, "a round of steps starts at slot 0");
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kStepBytes];
+    __shared__ float s_dmax[2][NW];  // per tile parity: each wave's max statistic
+    enum : int { kStepK = 0, kStepR = 1, kStepNop = 2, kStepEnd = 3 };
+    // step descriptor: kind | st << 2 | (tile - t0) << 4 (loads only)
+
+    // The step sequence, produced kAhead steps before each step runs; all
+    // waves produce the same sequence (scalar state, the decision read from
+    // LDS made scalar).  kept_bits collects the decisions (T <= 64).
+    int gu = 0, gj = 0, gkept = 0;
+    unsigned long long kept_bits = 0;
+    auto next_step = [&]() __attribute__((always_inline)) -> int {
+      if (gu > T) return kStepEnd;
+      if (gj < 3) {
+        const int d = gu < T ? (kStepK | (gj << 2) | (gu << 4)) : kStepNop;
+        ++gj;
+        return d;
+      }
+      if (gj == 3 && gu >= 1) {
+        float dm = s_dmax[(gu - 1) & 1][0];
+#pragma unroll
+        for (int j = 1; j < NW; ++j) dm = fmaxf(dm, s_dmax[(gu - 1) & 1][j]);
+        gkept = __builtin_amdgcn_readfirstlane(!(dm < a.log2_thr) ? 1 : 0);
+        if (gkept) kept_bits |= 1ull << (gu - 1);
+      } else if (gj == 3) {
+        gkept = 0;
+      }
+      if (gkept && gj < 7) {
+        const int d = kStepR | ((gj - 3) << 2) | ((gu - 1) << 4);
+        ++gj;
+        return d;
+      }
+      const int d = gu < T ? (kStepK | (3 << 2) | (gu << 4)) : kStepEnd;
+      ++gu;
+      gj = 0;
+      return d;
+    };
+    auto load_step = [&](int d, int slot_i) __attribute__((always_inline)) {
+      // empty and end steps load the last step again (from L2), so every
+      // step issues the same loads and the waits below count them alike
+      const bool real = (d & 3) < kStepNop;
+      issue(t0 + (real ? d >> 4 : T - 1), real ? (d >> 2) & 3 : kStepsPerTile - 1,
+            ring + slot_i * kStepBytes);
+    };
+
+    float mrun = neg_inf();  // running max of head myhead over the decided tiles (log2 units)
+    float tmax = neg_inf();  // its max over the current tile's score steps
+    auto score_step = [&](const unsigned char* sl, int u, int st) __attribute__((always_inline)) {
+      f32x16_t s = scores(sl);
+      mask_tail(s, (t0 + u) * kTile + st * kStepKeys);
+      tmax = fmaxf(tmax, head_max(s));
+      if (st == kStepsPerTile - 1) {
+        float dh = neg_inf();
+        if (tmax != neg_inf()) dh = mrun == neg_inf() ? pos_inf() : tmax - mrun;
+        mrun = fmaxf(mrun, tmax);
+        tmax = neg_inf();
+        dh = wave_max(dh);
+        if (lane == 0) s_dmax[u & 1][w] = dh;
+      }
+    };
+    auto reread_step = [&](const unsigned char* sl, int u, int st) __attribute__((always_inline)) {
+      f32x16_t s = scores(sl);
+      mask_tail(s, (t0 + u) * kTile + st * kStepKeys);
+      accumulate(s, mref == neg_inf() ? 0.f : mref, sl);
+    };
+
+    // One ring step at slot I: wait for its loads, barrier, issue the loads
+    // of the step kAhead later, run it.  The slot's offset is hidden from the
+    // optimiser: as a constant, every slot's lane addresses would be hoisted
+    // out of the loop, four sets of them live at once.
+    auto step = [&](auto I, auto&& run) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      wait_vmcnt<(kAhead - 1) * LPW>();  // this step's loads have landed
+      lds_barrier();  // everyone's have, and everyone is done with the step before
+      load_step(next_step(), (i + kAhead) % kRing);
+      int off = i * kStepBytes;
+      asm volatile("" : "+s"(off));
+      run(ring + off);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+
+    // The exponent reference of a head is its running max at the first kept
+    // tile (tile 0); p = exp2(s - mref) then stays below 2^kStreamMargin
+    // while the running max (which bounds every kept score) stays within
+    // that margin of it -- fp32 and bf16 hold such p and their sums over a
+    // chain exactly as well as p <= 1.  A head whose running max climbs
+    // further sets s_restart: the pass runs again with every head's max over
+    // the chain as its reference (same decisions, no p above 1).
+    for (bool preset = false;; preset = true) {
+      if (tid == 0) s_restart = 0;
+#pragma unroll
+      for (int vb = 0; vb < kVb; ++vb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[vb][i] = 0.f;
+      lpart = 0.f;
+      gu = gj = gkept = 0;
+      kept_bits = 0;
+      mrun = tmax = neg_inf();
+      __syncthreads();
+      load_step(next_step(), 0);
+      load_step(next_step(), 1);
+      load_step(next_step(), 2);
+      // Round u (u <= T) runs K(u, 0..2) (empty steps for u = T), then R(u - 1,
+      // 0..3) if tile u - 1 was kept, then K(u, 3) (u < T).  A round takes 4 or
+      // 8 steps, so it always starts at slot 0.
+      for (int u = 0; u <= T; ++u) {
+        const bool real = u < T;
+        step(S0{}, [&](const unsigned char* sl) __attribute__((always_inline)) {
+          if (real) score_step(sl, u, 0);
+        });
+        step(S1{}, [&](const unsigned char* sl) __attribute__((always_inline)) {
+          if (real) score_step(sl, u, 1);
+        });
+        step(S2{}, [&](const unsigned char* sl) __attribute__((always_inline)) {
+          if (real) score_step(sl, u, 2);
+        });
+        // gkept: tile u - 1's decision, read by next_step at the barrier of
+        // this round's first step
+        if (gkept) {
+          if (!preset && mref == neg_inf()) mref = mrun;
+          if (__builtin_amdgcn_ballot_w64(mrun > mref + kStreamMargin) != 0 && lane == 0)
+            s_restart = 1;
+          step(S3{}, [&](const unsigned char* sl) __attribute__((always_inline)) {
+            reread_step(sl, u - 1, 0);
+          });
+          step(S0{}, [&](const unsigned char* sl) __attribute__((always_inline)) {
+            reread_step(sl, u - 1, 1);
+          });
+          step(S1{}, [&](const unsigned char* sl) __attribute__((always_inline)) {
+            reread_step(sl, u - 1, 2);
+          });
+          step(S2{}, [&](const unsigned char* sl) __attribute__((always_inline)) {
+            reread_step(sl, u - 1, 3);
+          });
+        }
+        if (real)
+          step(S3{}, [&](const unsigned char* sl) __attribute__((always_inline)) {
+            score_step(sl, u, 3);
+          });
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (s_restart == 0) break;
+      mref = mrun;      // the head's max over the chain
+      __syncthreads();  // everyone has read s_restart before it is cleared
+    }
+    if (a.mask && tid < T) a.mask[(size_t)pair * nK + t0 + tid] = (kept_bits >> tid) & 1ull ? 0 : 1;
+  } else {
   if constexpr (SHARE) {
     // the share the planning launch gave this workgroup
     const size_t us = (size_t)pair * S + sub;
@@ -553,6 +738,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
       __syncthreads();  // everyone has read s_restart
     }
   }
+  }
 
   // ------------------------------------------------------------ write O / l and lse
   const float l = sum_xor32(lpart);
@@ -686,7 +872,8 @@ int decode_mla_max_tiles(int) { return kTmax; }
 
 int decode_mla_workgroups_per_split(int) { return 1; }
 
-// Threshold 0, or few tiles per sub-split: one launch.  Otherwise three on
+// A threshold and sub-splits that are whole chains: one launch in stream
+// mode.  Threshold 0, or few tiles per sub-split: one launch.  Otherwise three on
 // the same stream: stage 1 scores every tile and decides (each sub-split
 // publishes its per-head maxima and its kept tiles), the planning launch
 // spreads each sequence's kept tiles evenly over its workgroups, stage 2 runs
@@ -708,20 +895,30 @@ hipError_t launch_decode_mla(const DecodeArgs& args, hipStream_t s) {
   // kept tiles (on 8 sequences of 16K / 32K keys, 4 / 8 tiles per
   // sub-split: 100 / 150 us in one launch, 121 / 164 us shared out; of
   // 64K / 128K keys, 16 / 32 tiles: 256 / 456 us against 229 / 365 us).
-  const bool share = a.tiles_per_split >= kShareMinTiles;
-  if (a.log2_thr == -__builtin_inff() || !share) {
+  const bool thresholded = a.log2_thr != -__builtin_inff();
+  if (thresholded && a.subs_per_chain == 1 && a.tiles_per_split <= kTmax) {
+    // every sub-split is a whole chain: one streaming pass, no look-back
     a.mla_stage = 0;
     if (G == 128)
-      hipLaunchKernelGGL((decode_mla_kernel<4, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_mla_kernel<4, kModeStream>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_mla_kernel<2, false>), grid, dim3(128), 0, s, a);
+      hipLaunchKernelGGL((decode_mla_kernel<2, kModeStream>), grid, dim3(128), 0, s, a);
+    return hipGetLastError();
+  }
+  const bool share = a.tiles_per_split >= kShareMinTiles;
+  if (!thresholded || !share) {
+    a.mla_stage = 0;
+    if (G == 128)
+      hipLaunchKernelGGL((decode_mla_kernel<4, kModeSplit>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_mla_kernel<2, kModeSplit>), grid, dim3(128), 0, s, a);
     return hipGetLastError();
   }
   a.mla_stage = 1;
   if (G == 128)
-    hipLaunchKernelGGL((decode_mla_kernel<4, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mla_kernel<4, kModeSplit>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_mla_kernel<2, false>), grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL((decode_mla_kernel<2, kModeSplit>), grid, dim3(128), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_mla_plan_kernel, dim3((unsigned)(args.B * args.Hkv)), dim3(256), 0, s,
@@ -730,9 +927,9 @@ hipError_t launch_decode_mla(const DecodeArgs& args, hipStream_t s) {
   if (e != hipSuccess) return e;
   a.mla_stage = 2;
   if (G == 128)
-    hipLaunchKernelGGL((decode_mla_kernel<4, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mla_kernel<4, kModeShare>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_mla_kernel<2, true>), grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL((decode_mla_kernel<2, kModeShare>), grid, dim3(128), 0, s, a);
   return hipGetLastError();
 }
 }  // namespace ssattn

@@ -293,6 +293,45 @@ def test_decode_mla_small(ss, case, mode):
     check_decode(ss, x, 1 / 24, thr, S, latent_dv=512, name=name, mode=mode)
 
 
+MLA_STREAM_CASES = [
+    # name, B, Hq, Lk, S, r, thr: every split a whole chain of at most 64
+    # tiles, so the decode runs as one streaming pass per split
+    ("mla128_one_chain_64_tiles", 2, 128, 8192, 1, 9.0, 0.05),
+    ("mla64_one_chain_ragged", 1, 64, 8192 - 37, 1, 9.0, 0.1),
+    ("mla128_four_chains", 3, 128, 5000, 4, 9.0, 0.05),
+    ("mla128_chains_thr1", 1, 128, 6000, 2, 9.0, 1.0),
+    ("mla64_chains_thr2", 2, 64, 4000, 3, 3.0, 2.0),
+    ("mla128_chains_dense_like", 1, 128, 3000, 2, 3.0, 1e-4),
+]
+
+
+@pytest.mark.parametrize("case", MLA_STREAM_CASES, ids=[c[0] for c in MLA_STREAM_CASES])
+def test_decode_mla_stream(ss, case):
+    name, B, Hq, Lk, S, r, thr = case
+    x = clustered_decode(zlib.crc32(name.encode()) % 10000, B, Hq, 1, Lk, 576, 512, 16, r,
+                         latent=True)
+    check_decode(ss, x, 1 / 24, thr, S, latent_dv=512, name=name, mode="independent")
+    if S == 1:
+        check_decode(ss, x, 1 / 24, thr, S, latent_dv=512, name=name, mode="chained")
+
+
+def test_decode_mla_stream_score_jump(ss):
+    """One chain of 64 tiles whose tile 40 scores about 60 nats above the rest
+    for every head: far beyond the range the streaming pass lets its
+    exponent reference trail the running max, so the pass runs again with
+    each head's max over the chain as reference.  The output is then carried
+    almost entirely by tile 40."""
+    x = clustered_decode(77, 1, 128, 1, 8192, 576, 512, 16, 9.0, latent=True)
+    u = x["q"][0].float().mean(0)
+    alpha = 60.0 * 24 / float(u @ u)
+    k = x["k"].float()
+    k[0, 0, 40 * 128:41 * 128] = 0.1 * k[0, 0, 40 * 128:41 * 128] + alpha * u
+    x["k"] = k.to(torch.bfloat16)
+    _, mask = check_decode(ss, x, 1 / 24, 0.05, 1, latent_dv=512, name="mla_score_jump",
+                           mode="independent")
+    assert mask[0, 0, 40] == 0
+
+
 @pytest.mark.parametrize("thr,mode", [(0.0, "chained"), (0.3, "chained"), (0.5, "independent")])
 def test_decode_mla_16k_full_size(ss, thr, mode):
     """Latent decode at full size (B8 Hq128 Lk16384, 576-wide latent rows,
