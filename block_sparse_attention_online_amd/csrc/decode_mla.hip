@@ -30,8 +30,9 @@
 // [32 keys x 64 columns] (128-byte rows); chunks are XOR-swizzled by row so
 // both read patterns hit distinct banks.
 //
-//  * threshold 0: one online pass (running max, rescale when it has grown by
-//    more than 2^8 -- P stays below 256, exactly representable scaling).
+//  * threshold 0: one online pass whose exponent reference trails the
+//    running max by at most 2^64 (see kRefMargin); the pass starts over only
+//    for a head whose scores climb further.
 //  * threshold > 0, sub-splits that are whole chains (independent splits, or
 //    one split): a single streaming pass (stream mode below).  Each tile is
 //    scored and decided against the running max of the tiles before it in
@@ -67,8 +68,11 @@ constexpr int kStepBytes = kRopeOff + kStepKeys * 128;   // 36 KB
 constexpr int kUnits = kStepBytes / 1024;                // 1 KB wave load instructions per step
 constexpr int kQk = kDqk / 16;                           // 36 MFMA k-steps over the key width
 constexpr int kVb = kDv / 32;                            // 16 value-column blocks
-constexpr float kRescaleMargin = 8.f;                    // log2 units (P < 256)
-constexpr float kStreamMargin = 64.f;                    // log2 units, stream mode
+// How far (log2 units) a head's scores may rise above its exponent reference
+// before a pass starts over: p = exp2(s - ref) then stays below 2^64, and its
+// sums over a sequence (at most 2^24 keys, |v| bf16) stay far below fp32's
+// 2^128; fp32 and bf16 carry such p with the same relative precision as p <= 1.
+constexpr float kRefMargin = 64.f;
 constexpr int kSpinCap = 1 << 21;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -518,10 +522,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
     using S3 = std::integral_constant<int, 3>;
 
     // The exponent reference of a head is its running max at the first kept
-    // tile (tile 0); p = exp2(s - mref) then stays below 2^kStreamMargin
-    // while the running max (which bounds every kept score) stays within
-    // that margin of it -- fp32 and bf16 hold such p and their sums over a
-    // chain exactly as well as p <= 1.  A head whose running max climbs
+    // tile (tile 0); p = exp2(s - mref) then stays below 2^kRefMargin while
+    // the running max (which bounds every kept score) stays within that
+    // margin of it.  A head whose running max climbs
     // further sets s_restart: the pass runs again with every head's max over
     // the chain as its reference (same decisions, no p above 1).
     for (bool preset = false;; preset = true) {
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
         // this round's first step
         if (gkept) {
           if (!preset && mref == neg_inf()) mref = mrun;
-          if (__builtin_amdgcn_ballot_w64(mrun > mref + kStreamMargin) != 0 && lane == 0)
+          if (__builtin_amdgcn_ballot_w64(mrun > mref + kRefMargin) != 0 && lane == 0)
             s_restart = 1;
           step(S3{}, [&](const unsigned char* sl) __attribute__((always_inline)) {
             reread_step(sl, u - 1, 0);
@@ -703,11 +706,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   } else {
     // ---------------------------------------------------------- online pass
     // The exponent reference of each head is its max over the first step;
-    // p = exp2(s - mref) may reach 2^8 (exact in fp32 and bf16 alike).  When
-    // some head's scores rise further above it, the pass starts over with
-    // every head's running max as its reference (rewriting the accumulators
-    // in place would cost a copy of all 256 of them through the vector ALU
-    // at every step; starting over happens only for score ranges above 2^8).
+    // p = exp2(s - mref) may reach 2^kRefMargin.  When some head's scores
+    // rise further above it, the pass starts over with every head's running
+    // max as its reference (rewriting the accumulators in place would cost a
+    // copy of all 256 of them through the vector ALU; with a reference 2^8
+    // wide, keys whose scores are i.i.d. Gumbel made every long pass start
+    // over, 456 against 279 us at 131072 keys).
     if (a.mask)
       for (int t = tid; t < T; t += kThreads) a.mask[(size_t)pair * nK + t0 + t] = 0;
     float mrun = neg_inf();  // running max of head myhead over the steps seen
@@ -726,7 +730,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
                  const float sm = head_max(s);
                  mrun = fmaxf(mrun, sm);
                  if (mref == neg_inf()) mref = sm;  // first step (always has a valid key)
-                 if (__builtin_amdgcn_ballot_w64(sm > mref + kRescaleMargin) != 0) {
+                 if (__builtin_amdgcn_ballot_w64(sm > mref + kRefMargin) != 0) {
                    if (lane == 0) s_restart = 1;
                  } else {
                    accumulate(s, mref, sl);
