@@ -12,8 +12,10 @@
       the dense-until point 0.7.
   python -m block_sparse_attention_online_amd.harness latent [--out FILE]
       latent decode (B8, 128 heads, 576-wide latent rows, value = first 512
-      columns) at 16K..128K keys: one factor a*exp(0.7 b) fitted so ~70 % of
-      tiles skip at every length; K bytes per second and MFMA rate.
+      columns) at 16K..128K keys, clustered keys (r = 3, r = 9) and keys with
+      i.i.d. Gumbel scores: one factor a*exp(0.7 b) fitted so ~70 % of tiles
+      skip at every length (chained splits), and the threshold bisected to
+      70 % with independent splits; K bytes per second and MFMA rate.
   python -m block_sparse_attention_online_amd.harness paged [--out FILE]
       paged decode of a serving-like batch (32 sequences of 1K..32K keys,
       Hq32/Hkv8, D128, 16-key cache blocks): one factor, threshold
@@ -253,16 +255,31 @@ def run_video(args):
 # --------------------------------------------------------------------------- latent decode
 
 def run_latent(args):
-    from synth import WORKLOADS, make_inputs
+    """Latent decode, 16K-128K keys, three key distributions (the clustered
+    generator at r = 3 and r = 9, and Gumbel scores): per length the
+    threshold bisected to 70 % skip with chained splits, the one factor a
+    (b from the sweep) that the method fits for all lengths, and the
+    threshold bisected to 70 % with independent splits (each split one
+    streaming pass), each timed against threshold 0."""
+    from synth import WORKLOADS, gumbel_decode, make_inputs
 
     timer, rows = Timer(), []
     ctxs = [16, 32, 64, 128]
     grid = [float(f"{t:.3g}") for t in np.logspace(-5, 0, 11)]
-    for r in (3.0, 9.0):
+
+    def clustered(r):
+        return lambda n: (WORKLOADS[f"mla_decode_{n}k"].replace(r=r),
+                          make_inputs(WORKLOADS[f"mla_decode_{n}k"].replace(r=r)))
+
+    def gumbel(n):
+        w = WORKLOADS[f"mla_decode_{n}k"]
+        return w, gumbel_decode(5100 + n, w.B, w.Hq, 1, w.Lk, 576, 512, w.scale, latent=True)
+
+    for keys, gen in (("clustered r=3", clustered(3.0)), ("clustered r=9", clustered(9.0)),
+                      ("gumbel", gumbel)):
         data, pts, per_ctx = {}, [], {}
         for n in ctxs:
-            w = WORKLOADS[f"mla_decode_{n}k"].replace(r=r)
-            x = make_inputs(w)
+            w, x = gen(n)
             q, k = x["q"].cuda(), x["k"].cuda()
             del x
             ws = torch.empty(ss_attn_decode_workspace_bytes(w.B, w.Hq, 1, w.Lk, 576, 512, 0),
@@ -270,16 +287,16 @@ def run_latent(args):
             mask = torch.empty(mask_shape_decode(w.B, 1, w.Lk), dtype=torch.uint8, device="cuda")
             out = torch.empty((w.B, w.Hq, 512), dtype=torch.bfloat16, device="cuda")
 
-            def part(thr, q=q, k=k, ws=ws, mask=mask, w=w):
+            def part(thr, mode, q=q, k=k, ws=ws, mask=mask, w=w):
                 ss_attn_decode_partial(q, k, None, dv=512, scale=w.scale, threshold=thr,
-                                       skip_mask=mask, workspace=ws)
+                                       skip_mask=mask, workspace=ws, split_mode=mode)
 
-            def call(thr, part=part, q=q, k=k, ws=ws, out=out):
-                part(thr)
+            def call(thr, mode="chained", part=part, q=q, k=k, ws=ws, out=out):
+                part(thr, mode)
                 ss_attn_decode_combine(q, k, ws, out, dv=512)
 
-            def skip_at(thr, part=part, mask=mask):
-                part(thr)
+            def skip_at(thr, mode="chained", part=part, mask=mask):
+                part(thr, mode)
                 torch.cuda.synchronize()
                 return skip_fraction(mask)
 
@@ -287,40 +304,43 @@ def run_latent(args):
                 s = skip_at(thr)
                 if 0.02 < s < 0.98:
                     pts.append((thr, w.Lk, s))
-            t70, s70, reach = bisect_threshold(skip_at, 0.7, iters=24, tol=0.005)
-            per_ctx[n] = (t70, s70, reach)
-            data[n] = (w, call, skip_at, mask, out, q, k, ws)
+            t70, _, reach = bisect_threshold(skip_at, 0.7, iters=24, tol=0.005)
+            i70, _, ireach = bisect_threshold(lambda t, f=skip_at: f(t, "independent"), 0.7,
+                                              iters=24, tol=0.005)
+            per_ctx[n] = (t70, reach, i70, ireach)
+            data[n] = (w, call, skip_at, mask, out)
         a_fit, b = fit_factor(pts) if len(pts) >= 2 else (float("nan"), 0.0)
         # one a for all lengths: ln a = mean over lengths of ln(t70 * L) - 0.7 b
-        la = [math.log(per_ctx[n][0] * data[n][0].Lk) - 0.7 * b for n in ctxs if per_ctx[n][2]]
+        la = [math.log(per_ctx[n][0] * data[n][0].Lk) - 0.7 * b for n in ctxs if per_ctx[n][1]]
         a = math.exp(sum(la) / len(la)) if la else float("nan")
-        emit({"workload": "mla_decode", "r": r, "stage": "fit", "b": float(f"{b:.6g}"),
+        emit({"keys": keys, "workload": "mla_decode", "stage": "fit", "b": float(f"{b:.6g}"),
               "a_sweep": float(f"{a_fit:.6g}"), "a_70": float(f"{a:.6g}"),
-              "contexts_reaching_0.7_at_thr_le_1": [n for n in ctxs if per_ctx[n][2]]}, rows)
+              "contexts_reaching_0.7_at_thr_le_1": [n for n in ctxs if per_ctx[n][1]]}, rows)
         for n in ctxs:
-            w, call, skip_at, mask, out, q, k, ws = data[n]
+            w, call, skip_at, mask, out = data[n]
             kbytes = w.B * w.Lk * 576 * 2
             dense_ms = timer.ms(lambda: call(0.0))
             dense_out = out.clone()
-            cases = [("bisected", per_ctx[n][0], per_ctx[n][2])]
+            t70, reach, i70, ireach = per_ctx[n]
+            cases = [("bisected", "chained", t70, reach)]
             if math.isfinite(a):
-                cases.append(("calibrated",) + calibrated_threshold(a, b, 0.7, w.Lk))
-            emit({"workload": f"mla_decode_{n}k", "r": r, "stage": "dense",
+                cases.append(("calibrated", "chained") + calibrated_threshold(a, b, 0.7, w.Lk))
+            cases.append(("bisected", "independent", i70, ireach))
+            emit({"keys": keys, "workload": f"mla_decode_{n}k", "stage": "dense",
                   "ms": round(dense_ms, 4), "k_gbs": round(kbytes / dense_ms / 1e6, 1),
                   "frac_hbm": round(kbytes / dense_ms / 1e6 / HBM_PEAK_GBS, 4)}, rows)
-            for kind, thr, reach in cases:
-                ms = timer.ms(lambda: call(thr))
-                s = skip_at(thr)
-                call(thr)
+            for kind, mode, thr, reach in cases:
+                ms = timer.ms(lambda: call(thr, mode))
+                s = skip_at(thr, mode)
+                call(thr, mode)
                 torch.cuda.synchronize()
                 m = mask.cpu().numpy()
-                keys = np.full(m.shape[-1], 128)
-                keys[-1] = w.Lk - 128 * (m.shape[-1] - 1)
-                kept_keys = int(((m == 0) * keys[None, None, :]).sum())
+                keys_per_tile = np.full(m.shape[-1], 128)
+                keys_per_tile[-1] = w.Lk - 128 * (m.shape[-1] - 1)
+                kept_keys = int(((m == 0) * keys_per_tile[None, None, :]).sum())
                 flops = 2.0 * w.Hq * (w.B * w.Lk * 576 + kept_keys * 512)
-                emit({"workload": f"mla_decode_{n}k", "r": r, "stage": kind,
-                      "threshold": float(f"{thr:.6g}"),
-                      "reachable": reach,
+                emit({"keys": keys, "workload": f"mla_decode_{n}k", "stage": kind,
+                      "split_mode": mode, "threshold": float(f"{thr:.6g}"), "reachable": reach,
                       "skip": round(s, 4), "ms": round(ms, 4),
                       "k_gbs": round(kbytes / ms / 1e6, 1),
                       "frac_hbm": round(kbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
@@ -330,8 +350,9 @@ def run_latent(args):
                       "rel_l2_vs_dense": float(f"{rel_l2_gpu(out, dense_out):.3e}")}, rows)
         del data
         torch.cuda.empty_cache()
-    cols = ["workload", "r", "stage", "threshold", "b", "a_70", "reachable", "skip", "ms",
-            "k_gbs", "frac_hbm", "mfma_tflops", "frac_bf16_peak", "speedup", "rel_l2_vs_dense"]
+    cols = ["keys", "workload", "stage", "split_mode", "threshold", "b", "a_70", "reachable",
+            "skip", "ms", "k_gbs", "frac_hbm", "mfma_tflops", "frac_bf16_peak", "speedup",
+            "rel_l2_vs_dense"]
     return rows, cols
 
 

@@ -267,22 +267,23 @@ def paged_decode(seed: int, lens, Hq: int, Hkv: int, D: int, Dv: int, n_c: int, 
 
 
 def gumbel_decode(seed: int, B: int, Hq: int, Hkv: int, Lk: int, D: int, Dv: int, scale: float,
-                  dtype: str = "bf16") -> dict:
+                  dtype: str = "bf16", latent: bool = False) -> dict:
     """Decode inputs whose scaled scores are i.i.d. standard Gumbel.
 
     Draw order, from the stream of each (b, kv head): the direction ``u``
     (normal, normalised), the scores ``g ~ Gumbel(0, 1)`` [Lk], the key noise
-    [Lk, D] (projected off ``u``), then V [Lk, Dv].  Every query head of the
-    group is ``q = u``; key ``i`` is ``(g_i / scale) * u + noise_i``, so
-    ``scale * q.k_i = g_i`` up to the rounding of the stored values.  With
-    ``dtype="bf16"`` the rounding moves a score by a few hundredths, with
-    ``"f32"`` by ~1e-6.
+    [Lk, D] (projected off ``u``), then V [Lk, Dv] (skipped when ``latent``:
+    the value rows are then the first ``Dv`` columns of each key row).  Every
+    query head of the group is ``q = u``; key ``i`` is
+    ``(g_i / scale) * u + noise_i``, so ``scale * q.k_i = g_i`` up to the
+    rounding of the stored values.  With ``dtype="bf16"`` the rounding moves a
+    score by a few hundredths, with ``"f32"`` by ~1e-6.
     """
     g_ = Hq // Hkv
     tdt = _torch_dtype(dtype)
     q = torch.empty((B, Hq, D), dtype=tdt)
     k = torch.empty((B, Hkv, Lk, D), dtype=tdt)
-    v = torch.empty((B, Hkv, Lk, Dv), dtype=tdt)
+    v = None if latent else torch.empty((B, Hkv, Lk, Dv), dtype=tdt)
 
     def unit(bh):
         b, hk = bh
@@ -295,7 +296,8 @@ def gumbel_decode(seed: int, B: int, Hq: int, Hkv: int, Lk: int, D: int, Dv: int
         kk = (g / scale)[:, None] * u[None, :] + noise
         q[b, hk * g_:(hk + 1) * g_] = _to_tensor(np.repeat(u[None, :], g_, axis=0), dtype)
         k[b, hk] = _to_tensor(kk, dtype)
-        v[b, hk] = _to_tensor(rng.standard_normal((Lk, Dv), dtype=np.float32), dtype)
+        if not latent:
+            v[b, hk] = _to_tensor(rng.standard_normal((Lk, Dv), dtype=np.float32), dtype)
 
     _for_units([(b, hk) for b in range(B) for hk in range(Hkv)], unit)
     return {"q": q, "k": k, "v": v}
