@@ -424,75 +424,82 @@ def bench_backward(ss, torch, args):
 
 def bench_latent(ss, torch, args):
     """Latent-cache decode at 131072 keys: threshold 0 against the threshold
-    calibrated to the target skip (chained splits); K bytes per second."""
+    bisected to the target skip, with chained splits (score pass, then the
+    kept tiles) and with independent splits (one streaming pass per split);
+    K bytes per second."""
     from block_sparse_attention_online_amd.calibrate import bisect_threshold, skip_fraction
     from synth import WORKLOADS, make_inputs
+    import numpy as np
 
     w = WORKLOADS["mla_decode_128k"]
     x = make_inputs(w)
     q, k = x["q"].cuda(), x["k"].cuda()
     del x
-    ws = torch.empty(ss.ss_attn_decode_workspace_bytes(w.B, w.Hq, 1, w.Lk, 576, 512, 0),
+    ws = torch.zeros(ss.ss_attn_decode_workspace_bytes(w.B, w.Hq, 1, w.Lk, 576, 512, 0),
                      dtype=torch.uint8, device="cuda")
     mask = torch.empty(ss.mask_shape_decode(w.B, 1, w.Lk), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.B, w.Hq, 512), dtype=torch.bfloat16, device="cuda")
 
-    def call(thr):
+    def call(thr, mode):
         ss.ss_attn_decode_partial(q, k, None, dv=512, scale=w.scale, threshold=thr,
-                                  skip_mask=mask, workspace=ws)
+                                  skip_mask=mask, workspace=ws, split_mode=mode)
         ss.ss_attn_decode_combine(q, k, ws, out, dv=512)
 
-    def skip_at(thr):
-        call(thr)
+    def skip_at(thr, mode):
+        call(thr, mode)
         torch.cuda.synchronize()
         return skip_fraction(mask)
 
-    if args.latent_threshold is not None:
-        thr, reachable = args.latent_threshold, True
-    else:
-        thr, _, reachable = bisect_threshold(skip_at, args.target_skip, iters=24, tol=0.005)
-
-    def timed(th):
+    def timed(th, mode):
         for _ in range(3):
-            call(th)
+            call(th, mode)
         steps = max(5, args.steps // 4)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for i, e in enumerate(evs):
             evict_caches(args.flush)
             e[0].record()
-            call(th)
+            call(th, mode)
             e[1].record()
         torch.cuda.synchronize()
         return sum(e[0].elapsed_time(e[1]) for e in evs) / steps
 
-    dense_ms = timed(0.0)
-    dense_out = out.clone()
-    ms = timed(thr)
-    err = rel_l2(torch, out, dense_out)
-    s = skip_at(thr)
-    import numpy as np
-
-    m = mask.cpu().numpy()
-    nK = m.shape[-1]
-    keys = np.full(nK, 128, dtype=np.int64)
-    keys[-1] = w.Lk - 128 * (nK - 1)
-    kept_keys = int(((m == 0) * keys[None, None, :]).sum())
     kbytes = w.B * w.Lk * 576 * 2
-    # MFMA work: Q.K^T over every key (576 wide), P.V over kept keys (512 wide)
-    flops = 2.0 * w.Hq * (w.B * w.Lk * 576 + kept_keys * 512)
     dense_flops = 2.0 * w.Hq * w.B * w.Lk * (576 + 512)
+    dense_ms = timed(0.0, "chained")
+    dense_out = out.clone()
+
+    def leg(mode, fixed):
+        if fixed is not None:
+            thr, reachable = fixed, True
+        else:
+            thr, _, reachable = bisect_threshold(lambda t: skip_at(t, mode), args.target_skip,
+                                                 iters=24, tol=0.005)
+        ms = timed(thr, mode)
+        err = rel_l2(torch, out, dense_out)
+        s = skip_at(thr, mode)
+        m = mask.cpu().numpy()
+        nK = m.shape[-1]
+        keys = np.full(nK, 128, dtype=np.int64)
+        keys[-1] = w.Lk - 128 * (nK - 1)
+        kept_keys = int(((m == 0) * keys[None, None, :]).sum())
+        # MFMA work: Q.K^T over every key (576 wide), P.V over kept keys (512 wide)
+        flops = 2.0 * w.Hq * (w.B * w.Lk * 576 + kept_keys * 512)
+        return {"split_mode": mode, "threshold": thr, "threshold_reaches_target": reachable,
+                "skip_fraction": round(s, 4), "ms": round(ms, 4),
+                "k_gbs": round(kbytes / ms / 1e6, 1),
+                "frac_of_hbm_peak": round(kbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                "mfma_tflops": round(flops / ms / 1e9, 1),
+                "frac_of_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                "speedup_vs_dense": round(dense_ms / ms, 3),
+                "rel_l2_vs_dense": float(f"{err:.3e}")}
+
     res = {"workload": f"{w.name} (B8 Hq128, one 576-wide latent head, value = first 512 "
-                       "columns)", "split_mode": "chained",
-           "threshold": thr, "threshold_reaches_target": reachable,
-           "skip_fraction": round(s, 4), "ms": round(ms, 4), "dense_ms": round(dense_ms, 4),
-           "k_gbs": round(kbytes / ms / 1e6, 1), "dense_k_gbs": round(kbytes / dense_ms / 1e6, 1),
-           "frac_of_hbm_peak": round(kbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                       "columns)",
+           "dense_ms": round(dense_ms, 4), "dense_k_gbs": round(kbytes / dense_ms / 1e6, 1),
            "dense_frac_of_hbm_peak": round(kbytes / dense_ms / 1e6 / HBM_PEAK_GBS, 4),
-           "mfma_tflops": round(flops / ms / 1e9, 1),
-           "frac_of_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
-           "dense_frac_of_bf16_peak": round(dense_flops / dense_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
-           "speedup_vs_dense": round(dense_ms / ms, 3),
-           "rel_l2_vs_dense": float(f"{err:.3e}")}
+           "dense_frac_of_bf16_peak": round(dense_flops / dense_ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+    res.update(leg("chained", args.latent_threshold))
+    res["independent"] = leg("independent", None)
     log(f"[latent] {res}")
     return res
 
