@@ -258,7 +258,14 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     for (int i = 0; i < 16; ++i) oacc[mb][i] = 0.f;
 
   const float c = a.scale * kLog2e;  // raw score -> log2 units
-  float m2 = neg_inf();              // running max of row rq (log2 units)
+  float m2 = neg_inf();              // running max of row rq (log2 units): the skip test
+  // Exponent reference of row rq (log2 units): l and O hold sums of
+  // exp2(s c - mref).  It follows m2 only once m2 has risen more than
+  // kRefMargin above it (p = exp2(s c - mref) < 2^kRefMargin, exact in fp32
+  // and bf16 alike), so l and O are rescaled rarely, not whenever a row's max
+  // grows a little.
+  constexpr float kRefMargin = 8.f;
+  float mref = neg_inf();
   float lpart = 0.f;                 // this lane's half of the row's denominator
 
   // Per-lane LDS offsets (the parts of the addresses that depend on the
@@ -359,22 +366,24 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     if (mask_writer && lane == 0) mrow[j] = skip ? 1 : 0;
 
     const float m2n = fmaxf(m2, tmax2);
-    // Rescale l and O when some row's running max grew (the factor is exactly
-    // 1 for every other row).  A kept tile can raise m; a skipped one only
-    // when threshold > 1 (with threshold <= 1 a skipped tile lies below every
+    // Move the exponent reference (and rescale l and O by the factor, exactly
+    // 1 for every other row) when some row's max has risen more than
+    // kRefMargin above it.  A kept tile can raise m; a skipped one only when
+    // threshold > 1 (with threshold <= 1 a skipped tile lies below every
     // row's m).  One place for both, so the accumulators keep one register
-    // assignment through the loop.
-    if (__builtin_amdgcn_ballot_w64(m2n != m2) != 0) {
-      // rows that have seen no key yet (m2 = m2n = -inf) take 0, not NaN
-      const float alpha = fast_exp2(m2 - (m2n == neg_inf() ? 0.f : m2n));
+    // assignment through the loop.  A row that has seen no key yet keeps
+    // mref = -inf (its l and O are 0; the first key moves it).
+    const bool up = m2n > mref + kRefMargin;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float alpha = up ? fast_exp2(mref - m2n) : 1.f;  // mref = -inf: 0
       lpart *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+      if (up) mref = m2n;
     }
     if (!skip) {
-      const float mref = (m2n == neg_inf()) ? 0.f : m2n;
       // per-row decisions: a row that failed its own test gets P = 0
-      const float mexp = (a.per_row && row_skip) ? pos_inf() : mref;
+      const float mexp = (a.per_row && row_skip) ? pos_inf() : (mref == neg_inf() ? 0.f : mref);
       // ---- per 32-key block: exponentials, then O^T += V^T P^T (two 16-key
       // steps, V^T operands from transpose reads).
       const int voff0 = dual_tr_off<D>(lane_id_fresh(), 0, 0);
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   const float l = sum_xor32(lpart);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (a.lse && row_ok && g == 0)
-    a.lse[(size_t)(b * a.Hq + head) * a.Lq + rq] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : neg_inf();
+    a.lse[(size_t)(b * a.Hq + head) * a.Lq + rq] = l > 0.f ? (mref + __log2f(l)) * kLn2 : neg_inf();
   unsigned short* op = static_cast<unsigned short*>(a.out) + ((size_t)(b * a.Hq + head) * a.Lq) * D;
   if (row_ok) {
 #pragma unroll
