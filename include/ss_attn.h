@@ -234,6 +234,13 @@ typedef enum { SS_SPLIT_CHAINED = 0, SS_SPLIT_INDEPENDENT = 1 } ss_split_mode;
  * Bijdragen", names MHA, GQA, MQA and MLA); (576, 512) with v == NULL and
  * Hq/Hkv in {64, 128} (a shared latent cache).
  *
+ * With a latent cache the value is part of the key row, so a skipped tile
+ * saves its exponentials and its P.V work but no bytes.  CHAINED splits score
+ * every tile of a sequence before any decision and then read the kept tiles
+ * again; INDEPENDENT splits (and a single split) run one streaming pass per
+ * split, which decides each tile as it is scored and reads a kept tile once
+ * more from the last-level cache, not from HBM.
+ *
  * ss_attn_decode is ss_attn_decode_ex with split_mode CHAINED.
  */
 int ss_attn_decode(const void* q, const void* k, const void* v, void* out, int B, int Hq,
