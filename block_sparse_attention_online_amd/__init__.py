@@ -451,22 +451,31 @@ def ss_attn_decode_ex(q, k, v=None, out=None, *, dv=None, scale=None, threshold=
 
 
 def ss_attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len,
-                         out=None, scale=None, factor=0.0, thresholds=None, num_splits=0,
-                         skip_mask=None, workspace=None, stream=None):
+                         out=None, dv=None, scale=None, factor=0.0, thresholds=None,
+                         num_splits=0, skip_mask=None, workspace=None, stream=None):
     """Skip-softmax decode over a block-paged cache with per-sequence lengths.
 
-    q [B,Hq,D] bf16; k_cache/v_cache [num_blocks,Hkv,block_size,D] bf16;
-    block_table int32 [B,max_blocks]; seq_lens int32 [B] (all GPU tensors).
-    Sequence b uses ``thresholds[b]`` (fp32 GPU tensor) when given, else
-    ``factor / seq_lens[b]``.  Returns ``out`` [B,Hq,D]; fills ``skip_mask``
+    q [B,Hq,D] bf16; k_cache [num_blocks,Hkv,block_size,D] bf16; v_cache the
+    same shape with Dv columns, or None for a latent cache whose value rows are
+    the first ``dv`` columns of the key rows; block_table int32
+    [B,max_blocks]; seq_lens int32 [B] (all GPU tensors).  Sequence b uses
+    ``thresholds[b]`` (fp32 GPU tensor) when given, else
+    ``factor / seq_lens[b]``.  Returns ``out`` [B,Hq,Dv]; fills ``skip_mask``
     (u8 [B,Hkv,ceil(max_seq_len/128)], 2 past a sequence's end) when given."""
-    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+    if q.dim() != 3 or k_cache.dim() != 4 or (v_cache is not None and v_cache.dim() != 4):
         raise ValueError("q must be [B, Hq, D] and the caches [num_blocks, Hkv, block_size, D]")
     B, Hq, D = q.shape
     nblk, Hkv, bs, Dk = k_cache.shape
-    if Dk != D or tuple(v_cache.shape[:3]) != (nblk, Hkv, bs):
-        raise ValueError(f"cache shapes k{tuple(k_cache.shape)} v{tuple(v_cache.shape)} vs q{tuple(q.shape)}")
-    Dv = v_cache.shape[3]
+    if v_cache is None:
+        if dv is None:
+            raise ValueError("a latent cache (v_cache=None) needs dv")
+        Dv = int(dv)
+    else:
+        if tuple(v_cache.shape[:3]) != (nblk, Hkv, bs):
+            raise ValueError(f"cache shapes k{tuple(k_cache.shape)} v{tuple(v_cache.shape)}")
+        Dv = v_cache.shape[3]
+    if Dk != D:
+        raise ValueError(f"cache shape k{tuple(k_cache.shape)} vs q{tuple(q.shape)}")
     if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
     dt = torch.bfloat16
@@ -483,8 +492,9 @@ def ss_attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     tptr = None if thresholds is None else _dev(thresholds, "thresholds", torch.float32)
+    vptr = None if v_cache is None else _dev(v_cache, "v_cache", dt)
     p = _DecodePagedParams(_dev(q, "q", dt), _dev(k_cache, "k_cache", dt),
-                           _dev(v_cache, "v_cache", dt), _dev(block_table, "block_table", torch.int32),
+                           vptr, _dev(block_table, "block_table", torch.int32),
                            _dev(seq_lens, "seq_lens", torch.int32), tptr, _dev(out, "out", dt),
                            B, Hq, Hkv, D, Dv, bs, block_table.shape[1], nblk, int(max_seq_len),
                            float(scale), float(factor), int(num_splits), mptr,

@@ -486,9 +486,10 @@ int ss_attn_decode_combine(const ss_decode_params* p, hipStream_t stream) {
 
 int ss_attn_decode_paged(const ss_decode_paged_params* p, hipStream_t stream) {
   if (!p) return fail(SS_ERR_INVALID_ARG, "params is null");
-  if (!p->q || !p->k_cache || !p->v_cache || !p->block_table || !p->seq_lens || !p->out)
-    return fail(SS_ERR_INVALID_ARG,
-                "q, k_cache, v_cache, block_table, seq_lens and out must be non-null");
+  if (!p->q || !p->k_cache || !p->block_table || !p->seq_lens || !p->out)
+    return fail(SS_ERR_INVALID_ARG, "q, k_cache, block_table, seq_lens and out must be non-null");
+  // v_cache == NULL: a latent cache, the value row is the first Dv columns of the key row
+  const bool latent = p->v_cache == nullptr;
   if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->D <= 0 || p->Dv <= 0 ||
       p->max_blocks_per_seq <= 0 || p->num_blocks <= 0 || p->max_seq_len <= 0)
     return fail(SS_ERR_INVALID_ARG, "sizes must be positive");
@@ -510,11 +511,18 @@ int ss_attn_decode_paged(const ss_decode_paged_params* p, hipStream_t stream) {
   if (!(p->factor >= 0.f) || !std::isfinite(p->factor))
     return fail(SS_ERR_INVALID_ARG, "factor must be finite and >= 0 (got %g)", (double)p->factor);
   const int group = p->Hq / p->Hkv;
-  if (decode_kernel(p->D, p->Dv, group, false) != DecodeKernel::kGqa)
+  const DecodeKernel kern = decode_kernel(p->D, p->Dv, group, latent);
+  if (!latent && kern != DecodeKernel::kGqa)
     return fail(SS_ERR_UNSUPPORTED, "paged decode supports D == Dv in {64, 128} and Hq/Hkv in "
                 "1..8, 16 or 32 (got D=%d Dv=%d group=%d)", p->D, p->Dv, group);
+  if (latent && kern != DecodeKernel::kMla)
+    return fail(SS_ERR_UNSUPPORTED, "paged latent decode supports D = 576, Dv = 512 and Hq/Hkv "
+                "in {64, 128} (got D=%d Dv=%d group=%d)", p->D, p->Dv, group);
+  if (latent && p->block_size < 32)
+    return fail(SS_ERR_UNSUPPORTED, "paged latent decode needs block_size 32, 64 or 128 (got %d)",
+                p->block_size);
   const DecodePlan pl =
-      plan_decode(p->B, p->Hq, p->Hkv, p->max_seq_len, p->D, p->Dv, false, p->num_splits, true);
+      plan_decode(p->B, p->Hq, p->Hkv, p->max_seq_len, p->D, p->Dv, latent, p->num_splits, true);
   if (!p->workspace || p->workspace_bytes < pl.bytes)
     return fail(SS_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", pl.bytes,
                 p->workspace_bytes, p->workspace ? "" : ", null");
@@ -551,7 +559,8 @@ int ss_attn_decode_paged(const ss_decode_paged_params* p, hipStream_t stream) {
   a.max_blocks = p->max_blocks_per_seq;
   a.num_blocks = p->num_blocks;
   a.mask_tiles = (int)ceil_div(p->max_seq_len, SS_TILE_KEYS);
-  hipError_t e = ssattn::launch_decode_gqa_paged(a, stream);
+  hipError_t e = latent ? ssattn::launch_decode_mla_paged(a, stream)
+                        : ssattn::launch_decode_gqa_paged(a, stream);
   if (e != hipSuccess) return hip_fail(e, "paged decode launch");
   e = ssattn::launch_decode_combine(a, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");

@@ -133,12 +133,19 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16_t& x, f32x16_t& y) {
 // of a thresholded decode (this workgroup's share of the sequence's kept
 // tiles, from the planning launch); kModeStream: the single streaming pass of
 // a thresholded decode whose sub-splits are whole chains.
+//
+// PAGED (kModeSplit, stage 0 only): the latent rows come from a
+// [num_blocks, Hkv, 2^block_log2, 576] cache through a per-sequence block
+// table (block size 32 or more, so the 32 keys of a ring step lie in one
+// block); sequence b has seq_lens[b] keys (a.Lk is their upper bound) and the
+// threshold thresholds[b], or factor / seq_lens[b].
 constexpr int kModeSplit = 0;
 constexpr int kModeShare = 1;
 constexpr int kModeStream = 2;
 
-template <int NW, int MODE>
+template <int NW, int MODE, bool PAGED = false>
 __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
+  static_assert(!PAGED || MODE == kModeSplit, "paged caches: one launch per decode");
   constexpr bool SHARE = MODE == kModeShare;
   constexpr int G = NW * kHeadsPerWave;  // heads per latent head
   constexpr int kThreads = 64 * NW;
@@ -154,6 +161,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   __shared__ int s_surv[kTmax];
   __shared__ int s_nsurv;
   __shared__ int s_restart;
+  __shared__ int s_blk[PAGED ? kTmax * kTile / 32 : 1];  // paged: this sub-split's cache blocks
 
   // block -> (batch, sub-split): sub-splits in order, so every look-back
   // waits only on lower blocks (dispatched first)
@@ -163,7 +171,17 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   const int pair = usub / S;  // b * Hkv + hk
   const int hk = pair % a.Hkv;
   const int b = pair / a.Hkv;
-  const int nK = (a.Lk + kTile - 1) / kTile;
+  // the sequence's length and threshold (paged: per sequence)
+  int Lk = a.Lk;
+  float log2_thr = a.log2_thr;
+  if constexpr (PAGED) {
+    Lk = min(max(a.seq_lens[b], 0), a.Lk);
+    const float thr = a.thresholds ? a.thresholds[b]
+                                   : (Lk > 0 ? (float)((double)a.factor / (double)Lk) : 0.f);
+    log2_thr = thr > 0.f ? (float)log2((double)thr) : neg_inf();
+  }
+  const int nK = (Lk + kTile - 1) / kTile;
+  const int mstride = PAGED ? a.mask_tiles : nK;  // mask entries per (batch, latent head)
   const int chain = sub / a.subs_per_chain;
   const int link = sub % a.subs_per_chain;
   const int chain_t0 = chain * a.chain_tiles;
@@ -183,6 +201,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   // 0: one launch; 1: scores, decisions, kept tiles recorded (no output);
   // 2: this workgroup's share of the sequence's kept tiles (the output)
   const int stage = a.mla_stage;
+  if constexpr (PAGED) {
+    // tiles of this sub-split's range past the sequence's end: not visited
+    const int t_end = min(min(t0 + a.tiles_per_split, chain_t0 + a.chain_tiles), a.mask_tiles);
+    if (a.mask)
+      for (int t = max(t0, t0 + T) + tid; t < t_end; t += kThreads)
+        a.mask[(size_t)pair * mstride + t] = 2;
+  }
   if (T == 0 && !SHARE && stage == 1) {  // an empty trailing link: no tile kept, nothing published
     if (tid == 0) a.kept_bits[(size_t)pair * S + sub] = 0ull;
     return;
@@ -196,9 +221,19 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
     return;
   }
 
-  const unsigned char* kp = static_cast<const unsigned char*>(a.k) + (size_t)pair * a.Lk * (kDqk * 2);
+  const unsigned char* kp = static_cast<const unsigned char*>(a.k) +
+                           (PAGED ? 0 : (size_t)pair * a.Lk * (kDqk * 2));
   const float c = a.scale * kLog2e;
-  const bool dense = a.log2_thr == neg_inf();
+  const bool dense = log2_thr == neg_inf();
+  // paged: the cache blocks of keys [t0 * 128, min((t0 + T) * 128, Lk)), block
+  // ids clamped into the cache
+  const int blk0 = PAGED ? (t0 * kTile) >> a.block_log2 : 0;
+  if constexpr (PAGED) {
+    const int nb = ((min((t0 + T) * kTile, Lk) - 1) >> a.block_log2) - blk0 + 1;
+    for (int i = tid; i < nb; i += kThreads)
+      s_blk[i] = min(max(a.block_table[(size_t)b * a.max_blocks + blk0 + i], 0), a.num_blocks - 1);
+    __syncthreads();
+  }
 
   // Q^T operands: lane holds head myhead, dims [16 ks + 8 g, +8) for ks < 36
   bf16x8_t qf[kQk];
@@ -222,9 +257,18 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
 
   auto issue = [&](int tile, int st, unsigned char* dst) __attribute__((always_inline)) {
     // a step that starts past Lk (tail tile) reads the last key row throughout
-    const int key0 = min(tile * kTile + st * kStepKeys, a.Lk - 1);
-    const int rlast = a.Lk - 1 - key0;  // last valid row of this step (>= 0)
-    const unsigned char* src = kp + (size_t)key0 * (kDqk * 2);
+    const int key0 = min(tile * kTile + st * kStepKeys, Lk - 1);
+    const int rlast = Lk - 1 - key0;  // last valid row of this step (>= 0)
+    const unsigned char* src;
+    if constexpr (PAGED) {
+      // the step's rows are consecutive rows of one cache block
+      const int blk = s_blk[(key0 >> a.block_log2) - blk0];
+      const size_t r = (((size_t)blk * a.Hkv + hk) << a.block_log2) +
+                       (key0 & ((1 << a.block_log2) - 1));
+      src = kp + r * (kDqk * 2);
+    } else {
+      src = kp + (size_t)key0 * (kDqk * 2);
+    }
     const int ln = lane_id_fresh();
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -311,11 +355,11 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
   // raw scores of keys past Lk -> -inf (only the tail step of a sequence;
   // the lane's key offset is computed there, not kept live across the loop)
   auto mask_tail = [&](f32x16_t& s, int key0) __attribute__((always_inline)) {
-    if (key0 + kStepKeys > a.Lk) {
+    if (key0 + kStepKeys > Lk) {
       const int k0 = key0 + 4 * (lane_id_fresh() >> 5);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (k0 + 8 * (i >> 2) + (i & 3) >= a.Lk) s[i] = neg_inf();
+        if (k0 + 8 * (i >> 2) + (i & 3) >= Lk) s[i] = neg_inf();
     }
   };
 
@@ -459,7 +503,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
         float dm = s_dmax[(gu - 1) & 1][0];
 #pragma unroll
         for (int j = 1; j < NW; ++j) dm = fmaxf(dm, s_dmax[(gu - 1) & 1][j]);
-        gkept = __builtin_amdgcn_readfirstlane(!(dm < a.log2_thr) ? 1 : 0);
+        gkept = __builtin_amdgcn_readfirstlane(!(dm < log2_thr) ? 1 : 0);
         if (gkept) kept_bits |= 1ull << (gu - 1);
       } else if (gj == 3) {
         gkept = 0;
@@ -585,7 +629,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
       mref = mrun;      // the head's max over the chain
       __syncthreads();  // everyone has read s_restart before it is cleared
     }
-    if (a.mask && tid < T) a.mask[(size_t)pair * nK + t0 + tid] = (kept_bits >> tid) & 1ull ? 0 : 1;
+    if (a.mask && tid < T) a.mask[(size_t)pair * mstride + t0 + tid] = (kept_bits >> tid) & 1ull ? 0 : 1;
   } else {
   if constexpr (SHARE) {
     // the share the planning launch gave this workgroup
@@ -675,13 +719,13 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
     if (w == 0) {
       const bool valid = lane < T;
       const float d = valid ? s_dtile[lane] : neg_inf();
-      const bool kept = valid && !(d < a.log2_thr);
+      const bool kept = valid && !(d < log2_thr);
       const unsigned long long bits = __ballot(kept);
       const int idx = __popcll(bits & ((1ull << lane) - 1ull));
       if (kept) s_surv[idx] = t0 + lane;
       if (lane == 0) s_nsurv = __popcll(bits);
       if (lane == 0 && stage == 1) a.kept_bits[(size_t)pair * S + sub] = bits;
-      if (valid && a.mask) a.mask[(size_t)pair * nK + t0 + lane] = kept ? 0 : 1;
+      if (valid && a.mask) a.mask[(size_t)pair * mstride + t0 + lane] = kept ? 0 : 1;
     }
     __syncthreads();
     if (stage == 1) return;  // the planning launch and stage 2 run the kept tiles
@@ -713,7 +757,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_mla_kernel(DecodeArgs a) {
     // wide, keys whose scores are i.i.d. Gumbel made every long pass start
     // over, 456 against 279 us at 131072 keys).
     if (a.mask)
-      for (int t = tid; t < T; t += kThreads) a.mask[(size_t)pair * nK + t0 + t] = 0;
+      for (int t = tid; t < T; t += kThreads) a.mask[(size_t)pair * mstride + t0 + t] = 0;
     float mrun = neg_inf();  // running max of head myhead over the steps seen
     for (;;) {
 #pragma unroll
@@ -934,6 +978,24 @@ hipError_t launch_decode_mla(const DecodeArgs& args, hipStream_t s) {
     hipLaunchKernelGGL((decode_mla_kernel<4, kModeShare>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((decode_mla_kernel<2, kModeShare>), grid, dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+// Paged, variable-length latent decode: one launch (chained sub-splits score,
+// decide and run their own kept tiles; each sequence its own length and
+// threshold), then the merge.
+hipError_t launch_decode_mla_paged(const DecodeArgs& args, hipStream_t s) {
+  const int G = args.Hq / args.Hkv;
+  if (G != 128 && G != 64) return hipErrorInvalidValue;
+  if (args.block_log2 < 5 || args.block_log2 > 7) return hipErrorInvalidValue;
+  if (args.tiles_per_split > kTmax) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((size_t)args.num_splits * args.B * args.Hkv));
+  DecodeArgs a = args;
+  a.mla_stage = 0;
+  if (G == 128)
+    hipLaunchKernelGGL((decode_mla_kernel<4, kModeSplit, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_mla_kernel<2, kModeSplit, true>), grid, dim3(128), 0, s, a);
   return hipGetLastError();
 }
 }  // namespace ssattn

@@ -51,8 +51,9 @@ struct DecodeArgs {
   unsigned lb_tag;                 // nonzero, unique per launch (wraps after 2^31)
   unsigned long long* lb_slot;     // [S][B][Hkv][G] (tag << 32) | float bits
   unsigned int* lb_timeouts;       // count of look-back waits that gave up
-  // Paged caches (GQA decode): k, v point at [num_blocks, Hkv, 2^block_log2, D]
-  // caches, sequence b has seq_lens[b] keys (Lk is their upper bound) whose
+  // Paged caches: k, v point at [num_blocks, Hkv, 2^block_log2, D] caches (a
+  // latent cache: k alone, v null), sequence b has seq_lens[b] keys (Lk is
+  // their upper bound) whose
   // blocks are block_table[b][...] ([B][max_blocks]), and its threshold is
   // thresholds[b], or factor / seq_lens[b] when thresholds is null.  The mask
   // has mask_tiles entries per (batch, KV head).
@@ -125,6 +126,7 @@ hipError_t launch_decode_gqa_paged(const DecodeArgs& a, hipStream_t s);
 bool decode_gqa_supported(int D, int Dv, int group, bool latent);
 int decode_gqa_max_tiles(int group);  // tiles a split may hold in chained mode
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_mla_paged(const DecodeArgs& a, hipStream_t s);
 bool decode_mla_supported(int D, int Dv, int group, bool latent);
 int decode_mla_max_tiles(int group);
 int decode_mla_workgroups_per_split(int group);

@@ -18,9 +18,11 @@
       70 % with independent splits; K bytes per second and MFMA rate.
   python -m block_sparse_attention_online_amd.harness paged [--out FILE]
       paged decode of a serving-like batch (32 sequences of 1K..32K keys,
-      Hq32/Hkv8, D128, 16-key cache blocks): one factor, threshold
-      factor / L_b per sequence, bisected so ~70 % of the batch's tiles skip;
-      skip per length bucket, bytes per second, speedup over threshold 0.
+      Hq32/Hkv8, D128, 16-key cache blocks), and of a latent-cache batch (16
+      sequences of 4K..64K keys, 128 heads on one 576-wide latent head,
+      64-key blocks): one factor, threshold factor / L_b per sequence,
+      bisected so ~70 % of the batch's tiles skip; skip per length bucket,
+      bytes per second, speedup over threshold 0.
   python -m block_sparse_attention_online_amd.harness decode [--out FILE]
       GQA decode (B16, Hq32/Hkv8, 32768 keys, D128): skip 0.5 / 0.7 / 0.9
       against threshold 0, chained splits.
@@ -407,31 +409,31 @@ def run_decode(args):
 
 # --------------------------------------------------------------------------- paged decode
 
-def run_paged(args):
+def _paged_batch(timer, rows, name, seed, lens, Hq, Hkv, D, Dv, bs, r, latent):
+    """Dense and ~70 % skip (one factor, threshold factor / L_b per sequence,
+    bisected over the batch) for one paged batch; skip per length bucket."""
     from synth import paged_decode
 
     from . import ss_attn_decode_paged
 
-    timer, rows = Timer(), []
-    rng = np.random.default_rng(7000)
-    lens = [int(x) for x in rng.integers(1024, 32769, size=32)]
-    Hq, Hkv, D, bs = 32, 8, 128, 16
     t = time.time()
-    x = paged_decode(7000, lens, Hq, Hkv, D, D, 64, 3.0, bs)
-    log(f"[paged] generated {sum(lens)} tokens in {time.time() - t:.1f}s")
-    q, kc, vc = x["q"].cuda(), x["k_cache"].cuda(), x["v_cache"].cuda()
+    x = paged_decode(seed, lens, Hq, Hkv, D, Dv, 64 if not latent else 256, r, bs, latent=latent)
+    log(f"[paged] {name}: generated {sum(lens)} tokens in {time.time() - t:.1f}s")
+    q, kc = x["q"].cuda(), x["k_cache"].cuda()
+    vc = None if latent else x["v_cache"].cuda()
     table, sl = x["block_table"].cuda(), x["seq_lens"].cuda()
     del x
     B, L = len(lens), max(lens)
-    ws = torch.empty(ss_attn_decode_workspace_bytes(B, Hq, Hkv, L, D, D, 0), dtype=torch.uint8,
+    ws = torch.empty(ss_attn_decode_workspace_bytes(B, Hq, Hkv, L, D, Dv, 0), dtype=torch.uint8,
                      device="cuda")
     mask = torch.empty(mask_shape_decode(B, Hkv, L), dtype=torch.uint8, device="cuda")
-    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device="cuda")
     scale = 1.0 / math.sqrt(D)
 
     def call(factor):
-        ss_attn_decode_paged(q, kc, vc, table, sl, max_seq_len=L, out=out, scale=scale,
-                             factor=factor, skip_mask=mask, workspace=ws)
+        ss_attn_decode_paged(q, kc, vc, table, sl, max_seq_len=L, out=out,
+                             dv=Dv if latent else None, scale=scale, factor=factor,
+                             skip_mask=mask, workspace=ws)
 
     def skip_at(factor):
         call(factor)
@@ -440,10 +442,11 @@ def run_paged(args):
 
     nK = [-(-n // 128) for n in lens]
     kb = sum(lens) * Hkv * D * 2
+    dense_bytes = kb if latent else kb + sum(lens) * Hkv * Dv * 2
     dense_ms = timer.ms(lambda: call(0.0))
     dense_out = out.clone()
-    emit({"workload": "paged_decode_32seq", "stage": "dense", "tokens": sum(lens),
-          "ms": round(dense_ms, 4), "gbs": round(2 * kb / dense_ms / 1e6, 1)}, rows)
+    emit({"workload": name, "stage": "dense", "tokens": sum(lens), "ms": round(dense_ms, 4),
+          "gbs": round(dense_bytes / dense_ms / 1e6, 1)}, rows)
     # skip is non-decreasing in the factor: bisect it in log space over the batch
     lo, hi = 1e-3, 1e6
     if skip_at(hi) < 0.7:
@@ -461,25 +464,43 @@ def run_paged(args):
     m = mask.cpu().numpy()
     kept_keys = 0
     per_bucket = {}
+    width = 8192 if not latent else 16384
     for b, n in enumerate(lens):
         keys = np.full(nK[b], 128)
         keys[-1] = n - 128 * (nK[b] - 1)
         mb = m[b, :, :nK[b]]
         kept_keys += int(((mb == 0) * keys[None, :]).sum())
-        bucket = f"{(n - 1) // 8192 * 8}K-{(n - 1) // 8192 * 8 + 8}K"
+        lo_k = (n - 1) // width * (width // 1024)
+        bucket = f"{lo_k}K-{lo_k + width // 1024}K"
         sk, vis = per_bucket.get(bucket, (0, 0))
         per_bucket[bucket] = (sk + int((mb == 1).sum()), vis + mb.size)
-    by = kb + kept_keys * D * 2
-    emit({"workload": "paged_decode_32seq", "stage": "sparse", "factor": float(f"{factor:.6g}"),
+    # latent: V is inside K, skipping saves no bytes
+    by = kb if latent else kb + kept_keys * Dv * 2
+    emit({"workload": name, "stage": "sparse", "factor": float(f"{factor:.6g}"),
           "skip": round(s, 4), "ms": round(ms, 4), "gbs": round(by / ms / 1e6, 1),
           "frac_hbm": round(by / ms / 1e6 / HBM_PEAK_GBS, 4), "speedup": round(dense_ms / ms, 3),
           "rel_l2_vs_dense": float(f"{rel_l2_gpu(out, dense_out):.3e}")}, rows)
     for bucket in sorted(per_bucket, key=lambda k: int(k.split("K")[0])):
         sk, vis = per_bucket[bucket]
-        emit({"workload": "paged_decode_32seq", "stage": "skip by length", "bucket": bucket,
+        emit({"workload": name, "stage": "skip by length", "bucket": bucket,
               "skip": round(sk / vis, 4)}, rows)
-    cols = ["stage", "tokens", "factor", "bucket", "skip", "ms", "gbs", "frac_hbm", "speedup",
-            "rel_l2_vs_dense"]
+    del q, kc, vc, table, sl, ws, mask, out
+    torch.cuda.empty_cache()
+
+
+def run_paged(args):
+    timer, rows = Timer(), []
+    rng = np.random.default_rng(7000)
+    lens = [int(x) for x in rng.integers(1024, 32769, size=32)]
+    _paged_batch(timer, rows, "paged_decode_32seq", 7000, lens, 32, 8, 128, 128, 16, 3.0, False)
+    # latent cache: 16 sequences of 4K-64K keys, 128 heads on one 576-wide
+    # latent head, 64-key blocks
+    rng = np.random.default_rng(7100)
+    lens = [int(x) for x in rng.integers(4096, 65537, size=16)]
+    _paged_batch(timer, rows, "paged_latent_decode_16seq", 7100, lens, 128, 1, 576, 512, 64, 3.0,
+                 True)
+    cols = ["workload", "stage", "tokens", "factor", "bucket", "skip", "ms", "gbs", "frac_hbm",
+            "speedup", "rel_l2_vs_dense"]
     return rows, cols
 
 

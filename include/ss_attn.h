@@ -337,7 +337,9 @@ int ss_attn_decode_noalloc(const void* q, const void* k, const void* v, void* ou
  *
  *   q            [B, Hq, D] bf16
  *   k_cache      [num_blocks, Hkv, block_size, D] bf16
- *   v_cache      [num_blocks, Hkv, block_size, Dv] bf16
+ *   v_cache      [num_blocks, Hkv, block_size, Dv] bf16, or NULL: a latent
+ *                cache, the value row of a key is the first Dv columns of
+ *                its key row (D = 576, Dv = 512, Hq/Hkv in {64, 128})
  *   block_table  int32 [B, max_blocks_per_seq]: cache block of each
  *                block_size-key block of a sequence (device memory)
  *   seq_lens     int32 [B]: keys of each sequence (device memory)
@@ -347,8 +349,10 @@ int ss_attn_decode_noalloc(const void* q, const void* k, const void* v, void* ou
  *   skip_mask_out u8 [B, Hkv, ceil(max_seq_len/128)] or NULL (written; 2 marks
  *                tiles past a sequence's end)
  *
- * Host-side checks: shapes as for ss_attn_decode (Dv = D), block_size in
- * {16, 32, 64, 128}, max_seq_len <= max_blocks_per_seq * block_size, factor
+ * Host-side checks: shapes as for ss_attn_decode (Dv = D with a v_cache),
+ * block_size in {16, 32, 64, 128} ({32, 64, 128} for a latent cache: the 32
+ * keys of one latent load step lie in one block), max_seq_len <=
+ * max_blocks_per_seq * block_size, factor
  * finite and >= 0, workspace of ss_attn_decode_workspace_bytes(B, Hq, Hkv,
  * max_seq_len, D, Dv, num_splits) bytes.  The device arrays are trusted up to
  * clamping: a sequence length is clamped into [0, max_seq_len] (0 writes a

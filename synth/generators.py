@@ -223,7 +223,8 @@ def video_dit_field(seed: int, B: int, H: int, grid: tuple = (13, 42, 60), n_fie
 
 
 def paged_decode(seed: int, lens, Hq: int, Hkv: int, D: int, Dv: int, n_c: int, r: float,
-                 block_size: int, dtype: str = "bf16", spare_blocks: int = 3) -> dict:
+                 block_size: int, dtype: str = "bf16", spare_blocks: int = 3,
+                 latent: bool = False) -> dict:
     """Variable-length decode inputs in a block-paged KV cache.
 
     Sequence i (length ``lens[i]``) is drawn as ``clustered_decode`` with seed
@@ -235,19 +236,21 @@ def paged_decode(seed: int, lens, Hq: int, Hkv: int, D: int, Dv: int, n_c: int, 
     block table ``[B, max_blocks]`` (int32, -1 past a sequence's end), the
     lengths (int32), the queries ``[B, Hq, D]``, and the contiguous
     per-sequence ``k_seqs[i] [Hkv, L_i, D]`` / ``v_seqs[i]`` for a reference
-    to read without any paging.
+    to read without any paging.  ``latent``: no V is drawn (``v_cache`` and
+    ``v_seqs`` are None; the value rows are the first ``Dv`` columns of the
+    key rows), as in ``clustered_decode``.
     """
     B = len(lens)
     tdt = _torch_dtype(dtype)
     seqs = [clustered_decode(int(np.random.SeedSequence([seed, i]).generate_state(1)[0] % (1 << 30)),
-                             1, Hq, Hkv, int(L), D, Dv, n_c, r, dtype=dtype)
+                             1, Hq, Hkv, int(L), D, Dv, n_c, r, latent=latent, dtype=dtype)
             for i, L in enumerate(lens)]
     nblk = [-(-int(L) // block_size) for L in lens]
     max_blocks = max(nblk)
     total = sum(nblk) + spare_blocks
     perm = np.random.default_rng([seed, 1 << 20]).permutation(total)
     k_cache = torch.zeros((total, Hkv, block_size, D), dtype=tdt)
-    v_cache = torch.zeros((total, Hkv, block_size, Dv), dtype=tdt)
+    v_cache = None if latent else torch.zeros((total, Hkv, block_size, Dv), dtype=tdt)
     table = np.full((B, max_blocks), -1, dtype=np.int32)
     nxt = 0
     for i, L in enumerate(lens):
@@ -255,14 +258,16 @@ def paged_decode(seed: int, lens, Hq: int, Hkv: int, D: int, Dv: int, n_c: int, 
         phys = torch.from_numpy(perm[nxt:nxt + n].astype(np.int64))
         nxt += n
         table[i, :n] = phys.numpy()
-        for src, dst in ((seqs[i]["k"][0], k_cache), (seqs[i]["v"][0], v_cache)):
+        pairs = [(seqs[i]["k"][0], k_cache)] + ([] if latent else [(seqs[i]["v"][0], v_cache)])
+        for src, dst in pairs:
             pad = torch.zeros((src.shape[0], n * block_size, src.shape[2]), dtype=tdt)
             pad[:, : int(L)] = src  # [Hkv, L, d] -> blocks [n, Hkv, block_size, d]
             dst.index_copy_(0, phys, pad.reshape(src.shape[0], n, block_size, src.shape[2])
                             .permute(1, 0, 2, 3).contiguous())
     return {"q": torch.cat([s_["q"] for s_ in seqs]), "k_cache": k_cache, "v_cache": v_cache,
             "block_table": torch.from_numpy(table), "seq_lens": torch.tensor(lens, dtype=torch.int32),
-            "k_seqs": [s_["k"][0] for s_ in seqs], "v_seqs": [s_["v"][0] for s_ in seqs]}
+            "k_seqs": [s_["k"][0] for s_ in seqs],
+            "v_seqs": None if latent else [s_["v"][0] for s_ in seqs]}
 
 
 

@@ -36,19 +36,21 @@ def log(*a):
     print(*a, flush=True)
 
 
-def run_paged(ss, x, scale, factor=0.0, thresholds=None, num_splits=0):
+def run_paged(ss, x, scale, factor=0.0, thresholds=None, num_splits=0, latent_dv=None):
     B, Hq, D = x["q"].shape
     Hkv = x["k_cache"].shape[1]
+    Dv = latent_dv or D
     L = int(x["seq_lens"].max())
     mask = torch.full(ss.mask_shape_decode(B, Hkv, L), 255, dtype=torch.uint8, device="cuda")
-    nbytes = ss.ss_attn_decode_workspace_bytes(B, Hq, Hkv, L, D, D, num_splits)
+    nbytes = ss.ss_attn_decode_workspace_bytes(B, Hq, Hkv, L, D, Dv, num_splits)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     thr_t = None if thresholds is None else torch.tensor(thresholds, dtype=torch.float32,
                                                          device="cuda")
+    v_cache = None if x["v_cache"] is None else x["v_cache"].cuda()
     out = ss.ss_attn_decode_paged(
-        x["q"].cuda(), x["k_cache"].cuda(), x["v_cache"].cuda(), x["block_table"].cuda(),
-        x["seq_lens"].cuda(), max_seq_len=L, scale=scale, factor=factor, thresholds=thr_t,
-        num_splits=num_splits, skip_mask=mask, workspace=ws)
+        x["q"].cuda(), x["k_cache"].cuda(), v_cache, x["block_table"].cuda(),
+        x["seq_lens"].cuda(), max_seq_len=L, dv=latent_dv, scale=scale, factor=factor,
+        thresholds=thr_t, num_splits=num_splits, skip_mask=mask, workspace=ws)
     torch.cuda.synchronize()
     timeouts = int(ws[nbytes - 256:nbytes - 252].view(torch.int32).item())
     return out.float().cpu().numpy(), mask.cpu().numpy(), timeouts
@@ -61,23 +63,24 @@ def seq_threshold(factor, thresholds, b, L):
     return float(np.float32(factor / L))
 
 
-def check_paged(ss, x, scale, name, factor=0.0, thresholds=None, num_splits=0):
-    out, mask, timeouts = run_paged(ss, x, scale, factor, thresholds, num_splits)
+def check_paged(ss, x, scale, name, factor=0.0, thresholds=None, num_splits=0, latent_dv=None):
+    out, mask, timeouts = run_paged(ss, x, scale, factor, thresholds, num_splits, latent_dv)
     assert timeouts == 0, f"{name}: {timeouts} look-back waits gave up"
     lens = [int(v) for v in x["seq_lens"]]
     skipped = visited = 0
     for b, L in enumerate(lens):
         thr = seq_threshold(factor, thresholds, b, L)
         qb = x["q"][b:b + 1]
-        kb, vb = x["k_seqs"][b][None], x["v_seqs"][b][None]
-        ref = oracle.decode(qb, kb, vb, scale, thr, 1)
+        kb = x["k_seqs"][b][None]
+        vb = None if x["v_seqs"] is None else x["v_seqs"][b][None]
+        ref = oracle.decode(qb, kb, vb, scale, thr, 1, latent_dv=latent_dv)
         nK = -(-L // 128)
         mb = mask[b:b + 1, :, :nK]
         assert np.isin(mb, (0, 1)).all(), f"{name}: sequence {b} has unwritten mask entries"
         assert (mask[b, :, nK:] == 2).all(), f"{name}: tiles past sequence {b}'s end not 2"
         gr = grade_masks(mb, ref["mask"], ref["delta"], thr, None)
         assert gr["ok"], f"{name}: sequence {b} mask {gr}"
-        forced = oracle.decode(qb, kb, vb, scale, thr, 1, force_mask=mb)
+        forced = oracle.decode(qb, kb, vb, scale, thr, 1, latent_dv=latent_dv, force_mask=mb)
         err = rel_l2(out[b:b + 1], forced["out"])
         assert err <= 1e-2, f"{name}: sequence {b} (L={L}, thr={thr:.3g}) rel-L2 {err}"
         row = max_row_rel_l2(out[b:b + 1], forced["out"])
@@ -108,6 +111,25 @@ def test_paged_decode(ss, case):
     name, lens, Hq, Hkv, D, bs, r, factor, thresholds, S = case
     x = paged_decode(zlib.crc32(name.encode()) % 10000, lens, Hq, Hkv, D, D, 16, r, bs)
     check_paged(ss, x, 1 / math.sqrt(D), name, factor, thresholds, S)
+
+
+PAGED_LATENT_CASES = [
+    # name, lengths, Hq, block_size, r, factor, thresholds, num_splits (one
+    # latent head: D = 576, value = the first 512 columns of the key row)
+    ("mla128_bs64_mixed", [3000, 129, 8197], 128, 64, 9.0, 300.0, None, 0),
+    ("mla64_bs32_per_seq", [2500, 1, 700], 64, 32, 9.0, 0.0, [0.05, 0.0, 1.0], 0),
+    ("mla128_bs128_dense", [1000, 2000], 128, 128, 3.0, 0.0, None, 0),
+    ("mla128_long_chain", [20000, 3000], 128, 64, 9.0, 400.0, None, 0),
+    ("mla64_splits", [5000, 300, 2600], 64, 32, 9.0, 150.0, None, 7),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_LATENT_CASES, ids=[c[0] for c in PAGED_LATENT_CASES])
+def test_paged_latent_decode(ss, case):
+    name, lens, Hq, bs, r, factor, thresholds, S = case
+    x = paged_decode(zlib.crc32(name.encode()) % 10000, lens, Hq, 1, 576, 512, 16, r, bs,
+                     latent=True)
+    check_paged(ss, x, 1 / 24, name, factor, thresholds, S, latent_dv=512)
 
 
 def test_paged_equals_contiguous_decode(ss):
