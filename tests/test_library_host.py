@@ -373,6 +373,12 @@ def paged_call(ss, **over):
     (dict(factor=-1.0), -1), (dict(factor=float("nan")), -1), (dict(scale=0.0), -1),
     (dict(Hq=9), -1), (dict(D=96, Dv=96), -2), (dict(Hq=48, Hkv=2), -2),
     (dict(ws=None), -4), (dict(wsb=64), -4),
+    # a latent cache (v_cache NULL): only D 576 / Dv 512 with 64 or 128 heads,
+    # blocks of 32 keys or more
+    (dict(vc=None), -2),
+    (dict(vc=None, Hq=128, Hkv=1, D=576, Dv=512, bs=16, mb=200), -2),
+    (dict(vc=None, Hq=96, Hkv=1, D=576, Dv=512, bs=64, mb=50), -2),
+    (dict(vc=None, Hq=128, Hkv=1, D=576, Dv=512, bs=64, mb=50, wsb=64), -4),
 ])
 def test_paged_decode_rejects_before_launch(ss, over, code):
     assert paged_call(ss, **over) == code
