@@ -1,0 +1,104 @@
+"""Randomised GPU parity sweep: seeded draws of shape, layout, threshold,
+visit order, split count and mode, checked against the fp64 oracle exactly as
+the hand-picked cases are (masks under the margin rule, outputs against the
+oracle with the GPU's mask forced, the per-row bound).  The draws are fixed by
+the seed below, so every run checks the same cases; they reach combinations
+the hand-picked lists do not name (odd group sizes with Lq != Lk, ragged tails
+at every tile offset, many-split chains, per-sequence thresholds)."""
+
+import math
+
+import numpy as np
+import pytest
+
+from synth import clustered_decode, clustered_prefill, paged_decode
+from tests.test_paged_gpu import check_paged
+from tests.test_parity_gpu import check_decode, check_prefill, ss  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+THRESHOLDS = [0.0, 1e-3, 0.01, 0.05, 0.3, 1.0, 2.0]
+
+
+def _draws(n, seed, fn):
+    rng = np.random.default_rng(seed)
+    return [fn(rng, i) for i in range(n)]
+
+
+def _prefill_case(rng, i):
+    Hkv = int(rng.integers(1, 3))
+    group = int(rng.choice([1, 2, 3, 4]))
+    return dict(seed=9000 + i, B=int(rng.integers(1, 3)), Hq=Hkv * group, Hkv=Hkv,
+                Lq=int(rng.integers(1, 1500)), Lk=int(rng.integers(1, 1500)),
+                D=int(rng.choice([64, 128])), causal=bool(rng.integers(0, 2)),
+                order=str(rng.choice(["ascending", "diag_first"])), r=float(rng.choice([3.0, 9.0])),
+                thr=float(rng.choice(THRESHOLDS)))
+
+
+def _decode_case(rng, i):
+    Hkv = int(rng.integers(1, 3))
+    group = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 16, 32]))
+    return dict(seed=9100 + i, B=int(rng.integers(1, 4)), Hq=Hkv * group, Hkv=Hkv,
+                Lk=int(rng.integers(1, 6000)), D=int(rng.choice([64, 128])),
+                S=int(rng.choice([0, int(rng.integers(1, 41))])),
+                mode=str(rng.choice(["chained", "independent"])), r=float(rng.choice([3.0, 9.0])),
+                thr=float(rng.choice(THRESHOLDS)))
+
+
+def _latent_case(rng, i):
+    return dict(seed=9200 + i, B=int(rng.integers(1, 3)), Hq=int(rng.choice([64, 128])),
+                Lk=int(rng.integers(1, 9000)), S=int(rng.choice([0, int(rng.integers(1, 13))])),
+                mode=str(rng.choice(["chained", "independent"])), r=float(rng.choice([3.0, 9.0])),
+                thr=float(rng.choice(THRESHOLDS)))
+
+
+def _paged_case(rng, i):
+    latent = bool(rng.integers(0, 2))
+    lens = [int(x) for x in rng.integers(1, 6000, size=int(rng.integers(1, 5)))]
+    if latent:
+        Hq, Hkv, D, Dv, bs = int(rng.choice([64, 128])), 1, 576, 512, int(rng.choice([32, 64, 128]))
+    else:
+        Hkv = int(rng.integers(1, 3))
+        Hq, D = Hkv * int(rng.choice([1, 2, 4, 5, 8])), int(rng.choice([64, 128]))
+        Dv, bs = D, int(rng.choice([16, 32, 64, 128]))
+    return dict(seed=9300 + i, lens=lens, Hq=Hq, Hkv=Hkv, D=D, Dv=Dv, bs=bs, latent=latent,
+                r=float(rng.choice([3.0, 9.0])), factor=float(rng.choice([0.0, 20.0, 200.0, 2000.0])),
+                S=int(rng.choice([0, int(rng.integers(1, 9))])))
+
+
+PREFILL = _draws(40, 1, _prefill_case)
+DECODE = _draws(40, 2, _decode_case)
+LATENT = _draws(16, 3, _latent_case)
+PAGED = _draws(16, 4, _paged_case)
+
+
+def _id(c):
+    return "-".join(f"{k}{v}" for k, v in c.items() if k != "seed")[:90]
+
+
+@pytest.mark.parametrize("c", PREFILL, ids=[_id(c) for c in PREFILL])
+def test_random_prefill(ss, c):
+    x = clustered_prefill(c["seed"], c["B"], c["Hq"], c["Hkv"], c["Lq"], c["Lk"], c["D"], c["D"],
+                          16, c["r"], "tile")
+    check_prefill(ss, x, 1 / math.sqrt(c["D"]), c["causal"], c["thr"], c["order"], "bf16",
+                  name=_id(c))
+
+
+@pytest.mark.parametrize("c", DECODE, ids=[_id(c) for c in DECODE])
+def test_random_decode(ss, c):
+    x = clustered_decode(c["seed"], c["B"], c["Hq"], c["Hkv"], c["Lk"], c["D"], c["D"], 16, c["r"])
+    check_decode(ss, x, 1 / math.sqrt(c["D"]), c["thr"], c["S"], name=_id(c), mode=c["mode"])
+
+
+@pytest.mark.parametrize("c", LATENT, ids=[_id(c) for c in LATENT])
+def test_random_latent_decode(ss, c):
+    x = clustered_decode(c["seed"], c["B"], c["Hq"], 1, c["Lk"], 576, 512, 16, c["r"], latent=True)
+    check_decode(ss, x, 1 / 24, c["thr"], c["S"], latent_dv=512, name=_id(c), mode=c["mode"])
+
+
+@pytest.mark.parametrize("c", PAGED, ids=[_id(c) for c in PAGED])
+def test_random_paged_decode(ss, c):
+    x = paged_decode(c["seed"], c["lens"], c["Hq"], c["Hkv"], c["D"], c["Dv"], 16, c["r"], c["bs"],
+                     latent=c["latent"])
+    check_paged(ss, x, 1 / math.sqrt(c["D"]), _id(c), c["factor"], None, c["S"],
+                latent_dv=c["Dv"] if c["latent"] else None)
