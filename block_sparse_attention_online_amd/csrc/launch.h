@@ -49,7 +49,7 @@ struct DecodeArgs {
   // Every sub-split publishes its per-row maxima and folds in those of the
   // earlier sub-splits of its chain before deciding.
   unsigned lb_tag;                 // nonzero, unique per launch (wraps after 2^31)
-  unsigned long long* lb_slot;     // [S][B][Hkv][G] (tag << 32) | float bits
+  unsigned long long* lb_slot;     // [B][Hkv][S][G] (tag << 32) | float bits
   unsigned int* lb_timeouts;       // count of look-back waits that gave up
   // Paged caches: k, v point at [num_blocks, Hkv, 2^block_log2, D] caches (a
   // latent cache: k alone, v null), sequence b has seq_lens[b] keys (Lk is
