@@ -159,9 +159,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
   //   dK^T += Q^T dS| LDS: Q rows of the next block
   // Scheduling barriers keep the compiler from hoisting a stage's reads
   // further (their registers would not fit).  `tlim`: the row offset within
-  // the tile, minus 4 g, below which this lane's P is 0 (-2^30 when every
-  // row sees every key of the wave's block).
-  auto pair_body = [&](int tlim, const unsigned char* Qs, const unsigned char* Ds,
+  // the tile, minus 4 g, below which this lane's P is 0; `masked`: some row
+  // of the tile does not see some key of the wave's block.
+  auto pair_body = [&](bool masked, int tlim, const unsigned char* Qs, const unsigned char* Ds,
                        const float* Rs) {
     u32x4_t qa[KS], da[KS];
     bf16x8_t tv[2][MB], tq[2][MB];
@@ -191,6 +191,17 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
       }
       __builtin_amdgcn_sched_barrier(0);
 
+      // Rows that do not see this lane's key: their scores become -inf, so
+      // P is exactly 0 there (the scale is positive).  A uniform branch, so
+      // the pairs that need no mask run no per-element test (the empty asm
+      // keeps the compiler from turning it into selects every pair runs).
+      if (masked) {
+        asm volatile("");
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii)
+          if (rb * 32 + 8 * (ii >> 2) + (ii & 3) < tlim) sacc[ii] = neg_inf();
+      }
+
       // ---- stage 2: dP; P from S
       f32x16_t dacc;
 #pragma unroll
@@ -201,8 +212,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
       float pv[16];
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
-        const float pe = fast_exp2(fmaf(sacc[ii], c2, -l4[ii >> 2][ii & 3]));
-        pv[ii] = rb * 32 + 8 * (ii >> 2) + (ii & 3) < tlim ? 0.f : pe;
+        pv[ii] = fast_exp2(fmaf(sacc[ii], c2, -l4[ii >> 2][ii & 3]));
       }
       bf16x8_t pb[2];
       bw_pack_b(pv, pb);
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
     const int r0 = (i_min + p % nI) * kTile;
     // every key of this wave's block visible to every row of the tile?
     const bool full = (j0 + w * 32 + 32 <= a.Lk) && (!a.causal || j0 + w * 32 + 31 <= r0 + shift);
-    pair_body(full ? -(1 << 30) : rmin - r0 - 4 * g, Qs, Ds, Rs);
+    pair_body(!full, rmin - r0 - 4 * g, Qs, Ds, Rs);
   };
 
   int next = 0;  // first candidate pair not yet scanned

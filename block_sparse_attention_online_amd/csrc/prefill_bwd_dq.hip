@@ -204,14 +204,21 @@ __global__ __launch_bounds__(64 * kDqRowWaves * NH, 1) void bwd_dq_kernel(Prefil
         const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vs + kb * 32 * ROW + (roff0 ^ (ks << 5)));
         dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), of[ks], dpt, 0, 0, 0);
       }
-      float sv[16];
-      const int kg = j0 + kb * 32 + 4 * g;
+      // Keys past the row's limit: their scores become -inf, so their
+      // exponentials are exactly 0 (the scale is positive).  A uniform
+      // branch: the tiles that need no mask run no per-element test (the
+      // empty asm keeps the compiler from turning the branch into selects
+      // that every tile would run).
+      if (need_mask) {
+        asm volatile("");
+        const int kg = j0 + kb * 32 + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pe = fast_exp2(fmaf(st[i], c2, -lse2));
-        if (need_mask && kg + (i >> 2) * 8 + (i & 3) > lim) pe = 0.f;
-        sv[i] = pe * (dpt[i] - delta);
+        for (int i = 0; i < 16; ++i)
+          if (kg + (i >> 2) * 8 + (i & 3) > lim) st[i] = neg_inf();
       }
+      float sv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(fmaf(st[i], c2, -lse2)) * (dpt[i] - delta);
       bf16x8_t sb[2];
       bw_pack_b(sv, sb);
       // ---- dQ^T += K^T dS^T over the block's two 16-key steps
