@@ -202,9 +202,18 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   // covers rows 1024 i / ROW further on, and the swizzle of its rows differs
   // from load 0's by XOR with chunk bits -- K (k_slot): bits 2-3, (i & 3) << 2
   // for D = 128, (i & 1) << 2 for D = 64; V (dual_slot): bits 0-1, i & 3 for
-  // D = 128, (i & 1) << 1 for D = 64.  kgo0 and vgo0 are formed at each issue from the lane index
-  // (a few instructions; held across the tile loop they would not fit in
-  // registers).  Only the last tile clamps rows.
+  // D = 128, (i & 1) << 1 for D = 64.  kgo0 and vgo0 are formed once and held
+  // across the tile loop, like the operand offsets below: every vector
+  // instruction taken out of the loop shortens it, since the vector work
+  // does not run beside the MFMAs.  Only the last tile clamps rows.
+  unsigned kgo0, vgo0;
+  {
+    const int ln = lane_id_fresh();
+    const int lr = ln / KCH, pc = ln % KCH;
+    const int r = w * LOADS * ROWS_PER_LOAD + lr;
+    kgo0 = (unsigned)r * ROW + ((unsigned)k_slot<D>(r, pc) << 4);     // an involution
+    vgo0 = (unsigned)r * ROW + ((unsigned)dual_slot<D>(r, pc) << 4);  // likewise
+  }
   auto issue_tile = [&](int j, int st) {
     const int j0 = j * kTile;
     const unsigned char* kt = reinterpret_cast<const unsigned char*>(kp) + (size_t)j0 * ROW;
@@ -212,11 +221,6 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     unsigned char* kd = kst[st] + w * LOADS * ROWS_PER_LOAD * ROW;
     unsigned char* vd = vst[st] + w * LOADS * ROWS_PER_LOAD * ROW;
     if (j0 + kTile <= a.Lk) {
-      const int ln = lane_id_fresh();
-      const int lr = ln / KCH, pc = ln % KCH;
-      const int r = w * LOADS * ROWS_PER_LOAD + lr;
-      const unsigned kgo0 = (unsigned)r * ROW + ((unsigned)k_slot<D>(r, pc) << 4);  // an involution
-      const unsigned vgo0 = (unsigned)r * ROW + ((unsigned)dual_slot<D>(r, pc) << 4);  // likewise
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const unsigned ko = (kgo0 ^ (unsigned)((D == 128 ? (i & 3) : (i & 1)) << 6)) + i * 1024u;
@@ -269,8 +273,9 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   float lpart = 0.f;                 // this lane's half of the row's denominator
 
   // Per-lane LDS offsets (the parts of the addresses that depend on the
-  // swizzle), formed from the lane index where they are used: held across the
-  // tile loop they would not fit in the registers of two waves per SIMD.
+  // swizzle), formed once from the lane index and held across the tile loop
+  // (koff0, voff0 below; formed at each use they cost ~30 vector
+  // instructions per tile, 4 % of the dense time).
   // K: row kb * 32 + l32, logical chunk 2 ks + g; the swizzle depends on the
   // row only through l32 (the row block is an immediate offset), and k-step
   // ks's offset is koff(0) ^ (ks << 5) (chunk 2 ks + g differs from chunk g in
@@ -285,6 +290,8 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   // image uses dual_slot, which keeps 32 lanes of a transpose read on
   // different banks (the swizzle it replaced did so for 16 lanes only).
 
+  const int koff0 = koff_now();
+  const int voff0 = dual_tr_off<D>(lane_id_fresh(), 0, 0);
   if (U > 0) issue_tile(stream_tile(0), 0);
 
   // one stream step, from ring stage u & 1; the row set works on it when it
@@ -308,7 +315,6 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     bool row_skip = false;
     if (active) {
     // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 rows
-    const int koff0 = koff_now();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -386,7 +392,6 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
       const float mexp = (a.per_row && row_skip) ? pos_inf() : (mref == neg_inf() ? 0.f : mref);
       // ---- per 32-key block: exponentials, then O^T += V^T P^T (two 16-key
       // steps, V^T operands from transpose reads).
-      const int voff0 = dual_tr_off<D>(lane_id_fresh(), 0, 0);
       auto read_v = [&](int kb, int half, u32x4_t (&dst)[MB]) {
         const unsigned char* va = Vs + (kb * 32 + half * 16) * ROW;
 #pragma unroll
