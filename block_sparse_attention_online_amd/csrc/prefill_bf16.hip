@@ -32,9 +32,10 @@
 //    operand comes from the row-major V tile through ds_read_b64_tr_b16
 //    transpose reads (each 16-lane group turns 4 keys x 16 value columns into
 //    4 keys per column).
-//  * The skip decision: per row delta = tile_max - m (log2 units), the max over
-//    the wave's 32 rows by DPP, the max over the head's 4 waves through LDS;
-//    skip when it is below log2(threshold).  The branch is uniform over the
+//  * The skip decision: per row delta = tile_max - m (log2 units); skip when
+//    the max of delta over the head's 128 rows is below log2(threshold), i.e.
+//    when no row passes its own test -- a ballot over each wave's rows, an OR
+//    over the head's 4 waves through LDS.  The branch is uniform over the
 //    head's waves, so a skipped tile issues no exp and no P.V MFMA at all.
 //    With per-row decisions the tile is still skipped exactly when every row
 //    fails the test; in a kept tile a row that fails it takes +inf as its
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   // for its loads itself (vmcnt 0 before the barrier at the top of a step).
   __shared__ __attribute__((aligned(1024))) unsigned char kst[2][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char vst[2][TILE_BYTES];
-  __shared__ float red[NH][kRowWaves];
+  __shared__ int red[NH][kRowWaves];  // per wave: some row of it passes its own test
 
   const int nQ = (a.Lq + kTile - 1) / kTile;
   const int tid = threadIdx.x;
@@ -360,15 +361,18 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     if (row_ok && tmax2 != neg_inf()) delta = (m2 == neg_inf()) ? pos_inf() : tmax2 - m2;
     row_skip = delta < a.log2_thr;  // this row's own test
     if (row_writer) rrow()[j] = row_skip ? 1 : 0;
-    delta = wave_max(delta);
-    if (lane == 0) red[hh][wr] = delta;
+    // The tile is skipped iff the max over the head's rows of delta is below
+    // log2(threshold), i.e. iff no row passes its own test: one ballot per
+    // wave, an OR over the head's waves (no max reduction across lanes).
+    const bool wave_keeps = __builtin_amdgcn_ballot_w64(!row_skip) != 0;
+    if (lane == 0) red[hh][wr] = wave_keeps ? 1 : 0;
     }
     __syncthreads();  // red[] visible
     if (active) {
-    float dblk = red[hh][0];
+    int keeps = red[hh][0];
 #pragma unroll
-    for (int i = 1; i < kRowWaves; ++i) dblk = fmaxf(dblk, red[hh][i]);
-    const bool skip = dblk < a.log2_thr;
+    for (int i = 1; i < kRowWaves; ++i) keeps |= red[hh][i];
+    const bool skip = keeps == 0;
     if (mask_writer && lane == 0) mrow[j] = skip ? 1 : 0;
 
     const float m2n = fmaxf(m2, tmax2);
