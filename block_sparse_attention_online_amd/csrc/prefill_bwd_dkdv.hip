@@ -37,6 +37,28 @@ namespace {
 
 constexpr int kDkdvWaves = 4;
 
+// S = Q K^T and dP = dO V^T in the MFMA's VGPR form.  The kernel needs more
+// than 256 registers per lane, so its builtin MFMAs accumulate in the
+// accumulation registers (AGPRs); S and dP are read by the vector ALU, and
+// from AGPRs every element would first take a v_accvgpr_read (128 per tile
+// pair).  These two chains are therefore written out (taking K and V as AGPR
+// operands instead spilled: both register files then filled up).  Gradients
+// are bitwise those of the builtin form; dense 4 % faster.  The hardware
+// forwards an accumulator from one MFMA to the next that names it (no wait); the first
+// MFMA of a chain starts from 0, two wait states after any vector write of
+// its operands; mfma_v_drain gives the 24 wait states an MFMA result needs
+// before a vector ALU instruction reads it, and ties the chain so that
+// nothing reads it earlier.
+__device__ __forceinline__ void mfma_v_first(f32x16_t& acc, u32x4_t a, bf16x8_t b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16_t& acc, u32x4_t a, bf16x8_t b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_drain(f32x16_t& x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwdArgs a) {
   constexpr int NW = kDkdvWaves;
@@ -174,22 +196,16 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
       // rows 8 (e / 4) + 4 g + e % 4)
       f32x16_t sacc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[ks]), kf[ks], sacc, 0, 0, 0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks == 0)
+          mfma_v_first(sacc, qa[0], kf[0]);
+        else
+          mfma_v(sacc, qa[ks], kf[ks]);
         da[ks] = *reinterpret_cast<const u32x4_t*>(Ds + rb * 32 * ROW + roff[ks]);
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        l4[q4] = *reinterpret_cast<const f32x4_t*>(Rs + rb * 32 + 8 * q4 + 4 * g);
-#pragma unroll
-      for (int x = 0; x < KS; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        if (ks < 4) l4[ks] = *reinterpret_cast<const f32x4_t*>(Rs + rb * 32 + 8 * ks + 4 * g);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      mfma_v_drain(sacc);
 
       // Rows that do not see this lane's key: their scores become -inf, so
       // P is exactly 0 there (the scale is positive).  A uniform branch, so
@@ -203,34 +219,28 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
       }
 
       // ---- stage 2: dP; P from S
+      // one dP MFMA, 16 / KS of P's elements and the next reads per step
+      // (KS k-steps: 2 h x MB transpose reads and the 4 Delta reads fit them)
+      static_assert(16 % KS == 0 && 2 * MB == KS && KS >= 4, "stage 2 layout");
       f32x16_t dacc;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) dacc[e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da[ks]), vf[ks], dacc, 0, 0, 0);
       float pv[16];
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        pv[ii] = fast_exp2(fmaf(sacc[ii], c2, -l4[ii >> 2][ii & 3]));
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks == 0)
+          mfma_v_first(dacc, da[0], vf[0]);
+        else
+          mfma_v(dacc, da[ks], vf[ks]);
+#pragma unroll
+        for (int ii = (16 / KS) * ks; ii < (16 / KS) * (ks + 1); ++ii)
+          pv[ii] = fast_exp2(fmaf(sacc[ii], c2, -l4[ii >> 2][ii & 3]));
+        tv[ks / MB][ks % MB] =
+            bw_tr_read(Ds + (rb * 32 + 16 * (ks / MB)) * ROW, toff[ks % MB][0], toff[ks % MB][1]);
+        if (ks < 4) d4[ks] = *reinterpret_cast<const f32x4_t*>(Rs + kTile + rb * 32 + 8 * ks + 4 * g);
+        __builtin_amdgcn_sched_barrier(0);
       }
       bf16x8_t pb[2];
       bw_pack_b(pv, pb);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          tv[h][mb] = bw_tr_read(Ds + (rb * 32 + 16 * h) * ROW, toff[mb][0], toff[mb][1]);
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        d4[q4] = *reinterpret_cast<const f32x4_t*>(Rs + kTile + rb * 32 + 8 * q4 + 4 * g);
-#pragma unroll
-      for (int x = 0; x < KS; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS read
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      mfma_v_drain(dacc);
 
       // ---- stage 3: dV^T += dO^T P; dS from dP
 #pragma unroll
