@@ -82,8 +82,13 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   constexpr int ROW = D * 2;                 // bytes per row
   constexpr int TILE_BYTES = kTile * ROW;    // one K or V tile
   constexpr int ROWS_PER_LOAD = 64 / KCH;    // rows one wave instruction covers
-  constexpr int LOADS = kTile / ROWS_PER_LOAD / NW;  // per wave per tile (each of K, V)
-  static_assert(LOADS >= 1 && LOADS * ROWS_PER_LOAD * NW == kTile, "tile split");
+  // The tile loads are issued by the waves of row set 0 only (one per SIMD):
+  // the loads a wave issues slow its own MFMA and vector work, so each SIMD
+  // keeps one wave that issues none (measured faster than spreading the loads
+  // over all waves or between the score blocks).
+  constexpr int LW = kRowWaves;                      // loading waves: 0 .. LW-1
+  constexpr int LOADS = kTile / ROWS_PER_LOAD / LW;  // per loading wave per tile (each of K, V)
+  static_assert(LOADS >= 1 && LOADS * ROWS_PER_LOAD * LW == kTile, "tile split");
 
   // Two-stage ring.  Its loads are direct-to-LDS loads written out in
   // assembly (dma16), which the compiler does not track: one loop body serves
@@ -193,8 +198,8 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   if (row_writer && plan.causal)
     for (int j = plan.last + 1; j < nK; ++j) rrow()[j] = 2;
 
-  // Issue the direct-to-LDS loads of tile j into ring stage st.  Wave w covers
-  // rows [w * LOADS * ROWS_PER_LOAD, ...); lane l of load i writes LDS row
+  // Issue the direct-to-LDS loads of tile j into ring stage st.  Loading wave
+  // w covers rows [w * LOADS * ROWS_PER_LOAD, ...); lane l of load i writes LDS row
   // (base row + l / KCH), physical chunk l % KCH, and fetches the logical
   // chunk that the swizzle puts there.  Rows past Lk read the last key row
   // (their scores are masked to -inf, their P is 0).
@@ -216,6 +221,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     vgo0 = (unsigned)r * ROW + ((unsigned)dual_slot<D>(r, pc) << 4);  // likewise
   }
   auto issue_tile = [&](int j, int st) {
+    if (w >= LW) return;
     const int j0 = j * kTile;
     const unsigned char* kt = reinterpret_cast<const unsigned char*>(kp) + (size_t)j0 * ROW;
     const unsigned char* vt = reinterpret_cast<const unsigned char*>(vp) + (size_t)j0 * ROW;
