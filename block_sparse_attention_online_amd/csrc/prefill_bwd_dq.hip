@@ -162,11 +162,16 @@ __global__ __launch_bounds__(64 * kDqRowWaves * NH, 1) void bwd_dq_kernel(Prefil
   const unsigned char* vbase = static_cast<const unsigned char*>(a.v) +
                                (size_t)(b * a.Hkv + hk) * a.Lk * ROW;
 
+  // With two waves per SIMD, the waves of the first head issue the loads (one
+  // per SIMD), so each SIMD keeps one wave that issues none: the loads a wave
+  // issues slow its own MFMA and vector work (as in the forward kernel).
+  constexpr int LW = NW > kDqRowWaves ? kDqRowWaves : NW;  // loading waves
   auto issue = [&](int e, unsigned char* kd, unsigned char* vd) {
+    if (w >= LW) return;
     const int j = e >> 2;
     const int rlast = a.Lk - 1 - j * kTile;
-    bw_issue_tile<D, NW>(kbase + (size_t)j * kTile * ROW, rlast, kd, w);
-    bw_issue_tile<D, NW>(vbase + (size_t)j * kTile * ROW, rlast, vd, w);
+    bw_issue_tile<D, LW>(kbase + (size_t)j * kTile * ROW, rlast, kd, w);
+    bw_issue_tile<D, LW>(vbase + (size_t)j * kTile * ROW, rlast, vd, w);
   };
 
   // One key tile (list entry t: tile << 2 | bit hh set when head hh kept it).
