@@ -4,14 +4,23 @@ the hand-picked cases are (masks under the margin rule, outputs against the
 oracle with the GPU's mask forced, the per-row bound).  The draws are fixed by
 the seed below, so every run checks the same cases; they reach combinations
 the hand-picked lists do not name (odd group sizes with Lq != Lk, ragged tails
-at every tile offset, many-split chains, per-sequence thresholds)."""
+at every tile offset, many-split chains, per-sequence thresholds).
+
+SSATTN_RANDOM_SCALE=n multiplies the number of draws and SSATTN_RANDOM_SEED=s
+moves every draw and input seed, for wider sweeps run by hand; the defaults
+give the fixed set above."""
 
 import math
+import os
 
 import numpy as np
 import pytest
 
-from synth import clustered_decode, clustered_prefill, paged_decode
+import oracle
+from oracle.grading import rel_l2
+from synth import clustered_decode, clustered_prefill, output_gradient, paged_decode
+from tests.test_backward_gpu import TOL as BWD_TOL
+from tests.test_backward_gpu import backward, forward
 from tests.test_paged_gpu import check_paged
 from tests.test_parity_gpu import check_decode, check_prefill, ss  # noqa: F401
 
@@ -66,10 +75,31 @@ def _paged_case(rng, i):
                 S=int(rng.choice([0, int(rng.integers(1, 9))])))
 
 
-PREFILL = _draws(40, 1, _prefill_case)
-DECODE = _draws(40, 2, _decode_case)
-LATENT = _draws(16, 3, _latent_case)
-PAGED = _draws(16, 4, _paged_case)
+def _backward_case(rng, i):
+    Hkv = int(rng.integers(1, 3))
+    group = int(rng.choice([1, 2, 3, 4]))
+    return dict(seed=9400 + i, B=int(rng.integers(1, 3)), Hq=Hkv * group, Hkv=Hkv,
+                Lq=int(rng.integers(1, 700)), Lk=int(rng.integers(1, 700)),
+                D=int(rng.choice([64, 128])), causal=bool(rng.integers(0, 2)),
+                thr=float(rng.choice([0.0, 0.01, 0.05, 0.3, 1.0])))
+
+
+SCALE = int(os.environ.get("SSATTN_RANDOM_SCALE", "1"))
+SEED = int(os.environ.get("SSATTN_RANDOM_SEED", "0"))
+
+
+def _set(n, seed, fn):
+    cases = _draws(n * SCALE, seed + 100 * SEED, fn)
+    for c in cases:
+        c["seed"] += 100000 * SEED
+    return cases
+
+
+PREFILL = _set(40, 1, _prefill_case)
+DECODE = _set(40, 2, _decode_case)
+LATENT = _set(16, 3, _latent_case)
+PAGED = _set(16, 4, _paged_case)
+BACKWARD = _set(12, 5, _backward_case)
 
 
 def _id(c):
@@ -102,3 +132,19 @@ def test_random_paged_decode(ss, c):
                      latent=c["latent"])
     check_paged(ss, x, 1 / math.sqrt(c["D"]), _id(c), c["factor"], None, c["S"],
                 latent_dv=c["Dv"] if c["latent"] else None)
+
+
+@pytest.mark.parametrize("c", BACKWARD, ids=[_id(c) for c in BACKWARD])
+def test_random_backward(ss, c):
+    x = clustered_prefill(c["seed"], c["B"], c["Hq"], c["Hkv"], c["Lq"], c["Lk"], c["D"], c["D"], 8,
+                          3.0, query_mode="tile")
+    do = output_gradient(5, c["B"], c["Hq"], c["Lq"], c["D"])
+    scale = 1.0 / math.sqrt(c["D"])
+    fwd = forward(ss, x, scale, c["causal"], c["thr"])
+    dq, dk, dv = backward(ss, fwd, do, scale, c["causal"])
+    mask = fwd[4].cpu().numpy()
+    ref = oracle.prefill_backward(x["q"], x["k"], x["v"], do, scale, c["causal"], mask)
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        e = rel_l2(g, ref[name])
+        assert np.isfinite(g).all(), (name, _id(c))
+        assert e <= BWD_TOL, (name, e, _id(c))
