@@ -20,20 +20,54 @@ constexpr int kMaskKept = 0;  // skip-mask byte of a tile the forward computed
 // workgroup share the tile's 1024-byte load instructions; lane l of a load
 // writes physical chunk l % (D / 8) of its row and so fetches the logical
 // chunk that dual_slot puts there.  Rows past `rlast` (>= 0) re-read row rlast.
+//
+// `go0` is the lane's source offset for load 0 (bw_issue_off0), formed once
+// per workgroup: load i of a full tile covers rows i * (64 / (D / 8)) further
+// on, 1024 bytes for D = 64 and 128, and the swizzle of its rows differs from
+// load 0's by XOR with chunk bits -- (i & 3) << 4 bytes for D = 128, (i & 1)
+// << 5 for D = 64 -- because dual_slot reads row bits 0-3 only and the
+// wave's first row is a multiple of 16.  Formed at each load, the offsets
+// cost about a fifth of the dK/dV kernel's vector instructions.
+template <int D, int NW>
+struct BwLoads {
+  static constexpr int ROW = 2 * D, KCH = D / 8, RPL = 64 / KCH, LOADS = kTile / RPL / NW;
+  static_assert(LOADS >= 1 && LOADS * RPL * NW == kTile, "tile split");
+  static_assert(RPL * ROW == 1024 && LOADS % (D == 128 ? 4 : 2) == 0, "offset step of a load");
+};
+
+template <int D, int NW>
+__device__ __forceinline__ unsigned bw_issue_off0(int w) {
+  using L = BwLoads<D, NW>;
+  const int ln = lane_id_fresh();
+  const int r = w * L::LOADS * L::RPL + ln / L::KCH;
+  return (unsigned)r * L::ROW + ((unsigned)dual_slot<D>(r, ln % L::KCH) << 4);
+}
+
 template <int D, int NW>
 __device__ __forceinline__ void bw_issue_tile(const unsigned char* src, int rlast,
-                                              unsigned char* dst, int w) {
-  constexpr int ROW = 2 * D, KCH = D / 8, RPL = 64 / KCH, LOADS = kTile / RPL / NW;
-  static_assert(LOADS >= 1 && LOADS * RPL * NW == kTile, "tile split");
-  const int ln = lane_id_fresh();
-  const int lr = ln / KCH, pc = ln % KCH;
+                                              unsigned char* dst, int w, unsigned go0) {
+  using L = BwLoads<D, NW>;
+  if (rlast >= kTile - 1) {
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int r = (w * LOADS + i) * RPL + lr;
-    const unsigned go = (unsigned)min(r, rlast) * ROW + ((unsigned)dual_slot<D>(r, pc) << 4);
+    for (int i = 0; i < L::LOADS; ++i) {
+      const unsigned go = (go0 ^ (unsigned)(D == 128 ? (i & 3) << 4 : (i & 1) << 5)) + i * 1024u;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(src + go),
+          (void __attribute__((address_space(3)))*)(dst + (w * L::LOADS + i) * L::RPL * L::ROW), 16,
+          0, 0);
+    }
+    return;
+  }
+  const int ln = lane_id_fresh();
+  const int lr = ln / L::KCH, pc = ln % L::KCH;
+#pragma unroll
+  for (int i = 0; i < L::LOADS; ++i) {
+    const int r = (w * L::LOADS + i) * L::RPL + lr;
+    const unsigned go = (unsigned)min(r, rlast) * L::ROW + ((unsigned)dual_slot<D>(r, pc) << 4);
     __builtin_amdgcn_global_load_lds(
         (const void __attribute__((address_space(1)))*)(src + go),
-        (void __attribute__((address_space(3)))*)(dst + (w * LOADS + i) * RPL * ROW), 16, 0, 0);
+        (void __attribute__((address_space(3)))*)(dst + (w * L::LOADS + i) * L::RPL * L::ROW), 16,
+        0, 0);
   }
 }
 

@@ -150,14 +150,15 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
 
   // Loads of pair p into one ring stage: Q_i and dO_i by all waves, the rows'
   // statistics (1 KiB) by wave 0.
+  const unsigned go0 = bw_issue_off0<D, NW>(w);
   auto issue = [&](int p, unsigned char* qd, unsigned char* dd, float* rd) {
     const int hl = p / nI;
     const int i = i_min + (p - hl * nI);
     const size_t bh = (size_t)b * a.Hq + hk * G + hl;
     const size_t r0 = bh * a.Lq + (size_t)i * kTile;
     const int rlast = a.Lq - 1 - i * kTile;
-    bw_issue_tile<D, NW>(static_cast<const unsigned char*>(a.q) + r0 * ROW, rlast, qd, w);
-    bw_issue_tile<D, NW>(static_cast<const unsigned char*>(a.dout) + r0 * ROW, rlast, dd, w);
+    bw_issue_tile<D, NW>(static_cast<const unsigned char*>(a.q) + r0 * ROW, rlast, qd, w, go0);
+    bw_issue_tile<D, NW>(static_cast<const unsigned char*>(a.dout) + r0 * ROW, rlast, dd, w, go0);
     if (w == 0) {
       const float* src = a.rowstat + (bh * nQ + i) * (2 * kTile) + 4 * lane_id_fresh();
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,

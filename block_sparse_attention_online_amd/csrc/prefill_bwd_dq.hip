@@ -166,12 +166,13 @@ __global__ __launch_bounds__(64 * kDqRowWaves * NH, 1) void bwd_dq_kernel(Prefil
   // per SIMD), so each SIMD keeps one wave that issues none: the loads a wave
   // issues slow its own MFMA and vector work (as in the forward kernel).
   constexpr int LW = NW > kDqRowWaves ? kDqRowWaves : NW;  // loading waves
+  const unsigned go0 = bw_issue_off0<D, LW>(w < LW ? w : 0);
   auto issue = [&](int e, unsigned char* kd, unsigned char* vd) {
     if (w >= LW) return;
     const int j = e >> 2;
     const int rlast = a.Lk - 1 - j * kTile;
-    bw_issue_tile<D, LW>(kbase + (size_t)j * kTile * ROW, rlast, kd, w);
-    bw_issue_tile<D, LW>(vbase + (size_t)j * kTile * ROW, rlast, vd, w);
+    bw_issue_tile<D, LW>(kbase + (size_t)j * kTile * ROW, rlast, kd, w, go0);
+    bw_issue_tile<D, LW>(vbase + (size_t)j * kTile * ROW, rlast, vd, w, go0);
   };
 
   // One key tile (list entry t: tile << 2 | bit hh set when head hh kept it).
