@@ -185,6 +185,28 @@ __device__ __forceinline__ void dma16(const void* gbase, unsigned goff, const un
       : "memory");
 }
 
+// Four such loads whose global and LDS addresses step by 1024 bytes: load x
+// (0..3) brings lane l's bytes at gbase + goff[x] + 1024 x to LDS address
+// lds + 1024 x + 16 l.  The instruction offset of a direct-to-LDS load moves
+// its global and its LDS address alike (observed on gfx950), so M0 is
+// written once for the four instead of twice per load.
+__device__ __forceinline__ void dma16_run4(const void* gbase, const unsigned (&goff)[4],
+                                           const unsigned char* lds) {
+  const unsigned la =
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)lds;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %6\n\t"
+      "global_load_lds_dwordx4 %3, %6 offset:1024\n\t"
+      "global_load_lds_dwordx4 %4, %6 offset:2048\n\t"
+      "global_load_lds_dwordx4 %5, %6 offset:3072\n\t"
+      "s_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "s"(la), "v"(goff[0]), "v"(goff[1]), "v"(goff[2]), "v"(goff[3]), "s"(gbase)
+      : "memory");
+}
+
 // ---- LDS tile swizzle for row and transpose reads --------------------------------
 
 // Physical 16-byte chunk of logical chunk c in row r of a tile image with

@@ -211,7 +211,9 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   // D = 128, (i & 1) << 1 for D = 64.  kgo0 and vgo0 are formed once and held
   // across the tile loop, like the operand offsets below: every vector
   // instruction taken out of the loop shortens it, since the vector work
-  // does not run beside the MFMAs.  Only the last tile clamps rows.
+  // does not run beside the MFMAs.  A full tile's loads go out in runs of
+  // four that share one M0 write (dma16_run4), each run's 1024-byte steps
+  // in the instruction offsets.  Only the last tile clamps rows.
   unsigned kgo0, vgo0;
   {
     const int ln = lane_id_fresh();
@@ -228,12 +230,18 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
     unsigned char* kd = kst[st] + w * LOADS * ROWS_PER_LOAD * ROW;
     unsigned char* vd = vst[st] + w * LOADS * ROWS_PER_LOAD * ROW;
     if (j0 + kTile <= a.Lk) {
+      // loads 4 h + x: offsets 4096 h in the bases, 1024 x in the instruction
+      static_assert(LOADS % 4 == 0 && ROWS_PER_LOAD * ROW == 1024, "load runs of four");
+      unsigned ko[4], vo[4];
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const unsigned ko = (kgo0 ^ (unsigned)((D == 128 ? (i & 3) : (i & 1)) << 6)) + i * 1024u;
-        dma16(kt, ko, kd + i * ROWS_PER_LOAD * ROW);
-        const unsigned vo = (vgo0 ^ (unsigned)(D == 128 ? (i & 3) << 4 : (i & 1) << 5)) + i * 1024u;
-        dma16(vt, vo, vd + i * ROWS_PER_LOAD * ROW);
+      for (int x = 0; x < 4; ++x) {
+        ko[x] = kgo0 ^ (unsigned)((D == 128 ? x : (x & 1)) << 6);
+        vo[x] = vgo0 ^ (unsigned)(D == 128 ? x << 4 : (x & 1) << 5);
+      }
+#pragma unroll
+      for (int h = 0; h < LOADS / 4; ++h) {
+        dma16_run4(kt + h * 4096, ko, kd + h * 4096);
+        dma16_run4(vt + h * 4096, vo, vd + h * 4096);
       }
     } else {
       const int rlast = a.Lk - 1 - j0;  // last valid row of this tile
