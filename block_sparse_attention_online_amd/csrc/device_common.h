@@ -286,14 +286,14 @@ struct VisitPlan {
   int nK;
   int causal;
   int diag_first;
+  // tile_at(t) = base + t, or base - t when `down`, less nK past the end
+  // (only a non-causal diag_first visit wraps): no branch on the order.
+  int base;
+  int down;
 
   __device__ __forceinline__ int tile_at(int t) const {
-    if (causal) return diag_first ? last - t : t;
-    if (diag_first) {
-      int j = start + t;
-      return j >= nK ? j - nK : j;
-    }
-    return t;
+    const int j = base + (down ? -t : t);
+    return j >= nK ? j - nK : j;
   }
 };
 
@@ -322,6 +322,10 @@ __device__ __forceinline__ VisitPlan make_visit_plan(int qtile, int Lq, int Lk, 
     if ((long)r0 + Lk - Lq < 0) s = 0;
     p.start = (int)min((long)(p.nK - 1), s);
   }
+  // visit orders: causal diag_first last, last - 1, ..., 0; non-causal
+  // diag_first start, ..., nK - 1, 0, ..., start - 1; ascending 0, 1, ...
+  p.down = causal && diag_first;
+  p.base = causal ? (diag_first ? p.last : 0) : (diag_first ? p.start : 0);
   return p;
 }
 
