@@ -32,8 +32,17 @@ template <int D, int NW>
 struct BwLoads {
   static constexpr int ROW = 2 * D, KCH = D / 8, RPL = 64 / KCH, LOADS = kTile / RPL / NW;
   static_assert(LOADS >= 1 && LOADS * RPL * NW == kTile, "tile split");
-  static_assert(RPL * ROW == 1024 && LOADS % (D == 128 ? 4 : 2) == 0, "offset step of a load");
+  static_assert(RPL * ROW == 1024 && LOADS % 4 == 0, "offset step of a load, runs of four");
 };
+
+// One direct-to-LDS load of 16 bytes per lane: src + goff + 1024 X to LDS
+// dst + 1024 X + 16 lane (X in the instruction offset).
+template <int X>
+__device__ __forceinline__ void bw_load16(const unsigned char* src, unsigned goff,
+                                          unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + goff),
+                                   (void __attribute__((address_space(3)))*)dst, 16, X * 1024, 0);
+}
 
 template <int D, int NW>
 __device__ __forceinline__ unsigned bw_issue_off0(int w) {
@@ -48,13 +57,18 @@ __device__ __forceinline__ void bw_issue_tile(const unsigned char* src, int rlas
                                               unsigned char* dst, int w, unsigned go0) {
   using L = BwLoads<D, NW>;
   if (rlast >= kTile - 1) {
+    // load 4 h + x: 4096 h in the addresses, 1024 x in the instruction offset,
+    // which moves the global and the LDS address alike (one M0 per four)
+    unsigned gx[4];
 #pragma unroll
-    for (int i = 0; i < L::LOADS; ++i) {
-      const unsigned go = (go0 ^ (unsigned)(D == 128 ? (i & 3) << 4 : (i & 1) << 5)) + i * 1024u;
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(src + go),
-          (void __attribute__((address_space(3)))*)(dst + (w * L::LOADS + i) * L::RPL * L::ROW), 16,
-          0, 0);
+    for (int x = 0; x < 4; ++x) gx[x] = go0 ^ (unsigned)(D == 128 ? x << 4 : (x & 1) << 5);
+    unsigned char* d0 = dst + w * L::LOADS * L::RPL * L::ROW;
+#pragma unroll
+    for (int h = 0; h < L::LOADS / 4; ++h) {
+      bw_load16<0>(src + h * 4096, gx[0], d0 + h * 4096);
+      bw_load16<1>(src + h * 4096, gx[1], d0 + h * 4096);
+      bw_load16<2>(src + h * 4096, gx[2], d0 + h * 4096);
+      bw_load16<3>(src + h * 4096, gx[3], d0 + h * 4096);
     }
     return;
   }
