@@ -347,15 +347,17 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
                                                             sacc[kb], 0, 0, 0);
       }
     }
-    if constexpr (!QP) {
-      // K operand reads issued eight MFMAs ahead of their use
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    {
+      // K operand reads issued RA MFMAs ahead of their use (fewer where the
+      // two-query-tile variant's registers run out)
+      constexpr int RA = QP ? 6 : 8;
+      __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
 #pragma unroll
-      for (int i = 0; i < 4 * KS - 8; ++i) {
+      for (int i = 0; i < 4 * KS - RA; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, RA, 0);
     }
 
     // ---- mask: keys past Lk, and causal keys past row + shift
