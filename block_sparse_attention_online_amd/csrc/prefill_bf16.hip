@@ -348,9 +348,10 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
       }
     }
     {
-      // K operand reads issued RA MFMAs ahead of their use (fewer where the
-      // two-query-tile variant's registers run out)
-      constexpr int RA = QP ? 6 : 8;
+      // K operand reads issued RA MFMAs ahead of their use: each MFMA then
+      // waits only for the read RA back, long since landed (four ahead,
+      // the compiler's own order, left every MFMA waiting on LDS)
+      constexpr int RA = 8;
       __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
 #pragma unroll
       for (int i = 0; i < 4 * KS - RA; ++i) {
