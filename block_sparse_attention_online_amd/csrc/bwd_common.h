@@ -16,7 +16,11 @@ constexpr int kBwdListCap = 2048;
 constexpr int kMaskKept = 0;  // skip-mask byte of a tile the forward computed
 
 // Direct-to-LDS loads of one 128-row tile (rows of D bf16 elements starting
-// at `src`) into the image at `dst`, swizzled by dual_slot.  The NW waves of the
+// at `src`, a wave-uniform address) into the image at `dst`, swizzled by
+// dual_slot.  Written out (dma16, dma16_run4), not through the compiler
+// builtin, which makes the compiler wait for every outstanding LDS read
+// (lgkmcnt 0) before each use of one; the kernels wait for these loads
+// themselves (s_waitcnt 0 before the ring's barrier).  The NW waves of the
 // workgroup share the tile's 1024-byte load instructions; lane l of a load
 // writes physical chunk l % (D / 8) of its row and so fetches the logical
 // chunk that dual_slot puts there.  Rows past `rlast` (>= 0) re-read row rlast.
@@ -34,15 +38,6 @@ struct BwLoads {
   static_assert(LOADS >= 1 && LOADS * RPL * NW == kTile, "tile split");
   static_assert(RPL * ROW == 1024 && LOADS % 4 == 0, "offset step of a load, runs of four");
 };
-
-// One direct-to-LDS load of 16 bytes per lane: src + goff + 1024 X to LDS
-// dst + 1024 X + 16 lane (X in the instruction offset).
-template <int X>
-__device__ __forceinline__ void bw_load16(const unsigned char* src, unsigned goff,
-                                          unsigned char* dst) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + goff),
-                                   (void __attribute__((address_space(3)))*)dst, 16, X * 1024, 0);
-}
 
 template <int D, int NW>
 __device__ __forceinline__ unsigned bw_issue_off0(int w) {
@@ -64,12 +59,7 @@ __device__ __forceinline__ void bw_issue_tile(const unsigned char* src, int rlas
     for (int x = 0; x < 4; ++x) gx[x] = go0 ^ (unsigned)(D == 128 ? x << 4 : (x & 1) << 5);
     unsigned char* d0 = dst + w * L::LOADS * L::RPL * L::ROW;
 #pragma unroll
-    for (int h = 0; h < L::LOADS / 4; ++h) {
-      bw_load16<0>(src + h * 4096, gx[0], d0 + h * 4096);
-      bw_load16<1>(src + h * 4096, gx[1], d0 + h * 4096);
-      bw_load16<2>(src + h * 4096, gx[2], d0 + h * 4096);
-      bw_load16<3>(src + h * 4096, gx[3], d0 + h * 4096);
-    }
+    for (int h = 0; h < L::LOADS / 4; ++h) dma16_run4(src + h * 4096, gx, d0 + h * 4096);
     return;
   }
   const int ln = lane_id_fresh();
@@ -78,10 +68,7 @@ __device__ __forceinline__ void bw_issue_tile(const unsigned char* src, int rlas
   for (int i = 0; i < L::LOADS; ++i) {
     const int r = (w * L::LOADS + i) * L::RPL + lr;
     const unsigned go = (unsigned)min(r, rlast) * L::ROW + ((unsigned)dual_slot<D>(r, pc) << 4);
-    __builtin_amdgcn_global_load_lds(
-        (const void __attribute__((address_space(1)))*)(src + go),
-        (void __attribute__((address_space(3)))*)(dst + (w * L::LOADS + i) * L::RPL * L::ROW), 16,
-        0, 0);
+    dma16(src, go, dst + (w * L::LOADS + i) * L::RPL * L::ROW);
   }
 }
 

@@ -159,11 +159,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(PrefillBwd
     const int rlast = a.Lq - 1 - i * kTile;
     bw_issue_tile<D, NW>(static_cast<const unsigned char*>(a.q) + r0 * ROW, rlast, qd, w, go0);
     bw_issue_tile<D, NW>(static_cast<const unsigned char*>(a.dout) + r0 * ROW, rlast, dd, w, go0);
-    if (w == 0) {
-      const float* src = a.rowstat + (bh * nQ + i) * (2 * kTile) + 4 * lane_id_fresh();
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void __attribute__((address_space(3)))*)rd, 16, 0, 0);
-    }
+    if (w == 0)
+      dma16(a.rowstat + (bh * nQ + i) * (2 * kTile), 16u * (unsigned)lane_id_fresh(),
+            reinterpret_cast<const unsigned char*>(rd));
   };
 
   // Rows of a tile that do not see this lane's key: r < rmin (causal: the key
