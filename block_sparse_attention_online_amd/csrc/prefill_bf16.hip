@@ -15,7 +15,9 @@
 //  * The NH heads visit the same key/value tiles in the same order, so every
 //    tile brought into LDS serves all of them; each head keeps its own
 //    128-row skip decision and its own running state.  With NH = 2 every SIMD
-//    runs two waves, so one wave's exponentials overlap the other's MFMAs.
+//    runs two waves, which cover each other's LDS and memory waits (they
+//    step through the same phases together, so one wave's exponentials do
+//    not run beside the other's MFMAs).
 //  * K and V tiles move from global memory straight into LDS
 //    (global_load_lds, 16 bytes per lane, no registers), into a two-stage
 //    ring: the next tile's loads are in flight while the current tile is
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(64 * kRowWaves * NH, 1) void prefill_bf16_kernel(Pr
   static_assert(LOADS >= 1 && LOADS * ROWS_PER_LOAD * LW == kTile, "tile split");
 
   // Two-stage ring.  Its loads are direct-to-LDS loads written out in
-  // assembly (dma16), which the compiler does not track: one loop body serves
+  // assembly (dma16_run4, dma16), which the compiler does not track: one loop body serves
   // both stages through a runtime stage base (no duplicated body, no copies of
   // the accumulators between two register assignments), and the ring waits
   // for its loads itself (vmcnt 0 before the barrier at the top of a step).
